@@ -1,1 +1,208 @@
-"""Lightweight DC attention on MI355X: Python binding (placeholder until the library exists)."""
+"""Lightweight DC (dynamically composable multi-head) attention on MI355X.
+
+Thin Python binding over the C ABI of libldc.so (include/ldc.h).  This module
+only marshals arguments: shapes, dtypes and device pointers of torch tensors,
+and the current HIP stream.  Every step of the layer runs in the HIP kernels;
+there is no fallback — if the library is missing the calls raise.
+
+    o = fwd(q, k, v, c, g, doc_ids)                 # [T,H,d]
+    dq, dk, dv, dc, dg = bwd(q, k, v, c, g, doc_ids, do)
+    o = ldc_attention(q, k, v, c, g, doc_ids)       # autograd-aware
+
+The layer is the one the AITNT page "一个国产AI小透明，连续两次刷新NanoGPT
+Speedrun世界纪录" describes in section "第二刀-砍层内" (Lightweight DC
+paragraph); the exact definition, with the readings taken where the page is
+silent, is in include/ldc.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = ["fwd", "bwd", "ldc_attention", "LDCFunction", "LDCError", "load_library",
+           "workspace_bytes", "status_str", "version", "LIB_PATH",
+           "LDC_BF16", "LDC_F32"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libldc.so")
+LDC_BF16, LDC_F32 = 0, 1
+DEFAULT_WINDOW = 112
+
+_lib = None
+
+
+class LDCError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libldc.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m dynamic_head_composition_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.ldc_fwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 8
+    lib.ldc_fwd.restype = i32
+    lib.ldc_bwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 12 + [vp, sz, vp]
+    lib.ldc_bwd.restype = i32
+    lib.ldc_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
+    lib.ldc_bwd_workspace_bytes.restype = sz
+    lib.ldc_status_str.argtypes = [i32]
+    lib.ldc_status_str.restype = ctypes.c_char_p
+    lib.ldc_version.argtypes = []
+    lib.ldc_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().ldc_status_str(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().ldc_version())
+
+
+def workspace_bytes(dtype: int, T: int, H: int, d: int, window: int = DEFAULT_WINDOW) -> int:
+    return int(load_library().ldc_bwd_workspace_bytes(dtype, T, H, d, window))
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor front end (PyTorch provides device memory and the stream only)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LDC_BF16
+    if t.dtype == torch.float32:
+        return LDC_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(q, k, v, c, g, doc, do=None):
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d]")
+    T, H, d = q.shape
+    for name, x in (("k", k), ("v", v)) + ((("do", do),) if do is not None else ()):
+        if x.shape != q.shape or x.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    for name, x in (("c", c), ("g", g)):
+        if x.shape != (T, H) or x.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [T, H]")
+    if doc.shape != (T,) or doc.dtype != torch.int32:
+        raise ValueError("doc_ids must be int32 [T]")
+    for name, x in (("q", q), ("k", k), ("v", v), ("c", c), ("g", g), ("doc_ids", doc)) + \
+            ((("do", do),) if do is not None else ()):
+        if not x.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if x.device != q.device:
+            raise ValueError(f"{name} is on another device")
+    return T, H, d
+
+
+def _stream(q, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def fwd(q, k, v, c, g, doc_ids, window: int = DEFAULT_WINDOW, scale: Optional[float] = None,
+        out=None, stream=None):
+    """O[t,h,:] of the layer, float32 [T,H,d].  Enqueued on `stream`
+    (default: torch's current stream), not synchronised."""
+    torch = _torch()
+    lib = load_library()
+    T, H, d = _check(q, k, v, c, g, doc_ids)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty(q.shape, dtype=torch.float32, device=q.device) if out is None else out
+    if o.shape != q.shape or o.dtype != torch.float32 or not o.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like q")
+    st = lib.ldc_fwd(_dtype_code(q), T, H, d, window, float(scale),
+                     q.data_ptr(), k.data_ptr(), v.data_ptr(), c.data_ptr(), g.data_ptr(),
+                     doc_ids.data_ptr(), o.data_ptr(), _stream(q, stream))
+    if st != 0:
+        raise LDCError(st, "ldc_fwd")
+    return o
+
+
+def bwd(q, k, v, c, g, doc_ids, do, window: int = DEFAULT_WINDOW, scale: Optional[float] = None,
+        out=None, workspace=None, stream=None):
+    """(dQ, dK, dV, dC, dG), all float32."""
+    torch = _torch()
+    lib = load_library()
+    T, H, d = _check(q, k, v, c, g, doc_ids, do)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        out = (torch.empty((T, H, d), **f32), torch.empty((T, H, d), **f32),
+               torch.empty((T, H, d), **f32), torch.empty((T, H), **f32), torch.empty((T, H), **f32))
+    dq, dk, dv, dc, dg = out
+    need = workspace_bytes(_dtype_code(q), T, H, d, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.ldc_bwd(_dtype_code(q), T, H, d, window, float(scale),
+                     q.data_ptr(), k.data_ptr(), v.data_ptr(), c.data_ptr(), g.data_ptr(),
+                     doc_ids.data_ptr(), do.data_ptr(),
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dc.data_ptr(), dg.data_ptr(),
+                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                     _stream(q, stream))
+    if st != 0:
+        raise LDCError(st, "ldc_bwd")
+    return dq, dk, dv, dc, dg
+
+
+def _make_function():
+    torch = _torch()
+
+    class LDCFunction(torch.autograd.Function):
+        """Autograd wrapper: forward = ldc_fwd, backward = ldc_bwd (gradients
+        are cast back to the input dtypes)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, c, g, doc_ids, window=DEFAULT_WINDOW, scale=None):
+            ctx.save_for_backward(q, k, v, c, g, doc_ids)
+            ctx.window, ctx.scale = window, scale
+            return fwd(q, k, v, c, g, doc_ids, window, scale).to(q.dtype)
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, c, g, doc = ctx.saved_tensors
+            dq, dk, dv, dc, dg = bwd(q, k, v, c, g, doc, do.contiguous().to(q.dtype), ctx.window, ctx.scale)
+            return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dc, dg, None, None, None
+
+    return LDCFunction
+
+
+_fn = None
+
+
+def __getattr__(name):
+    global _fn
+    if name == "LDCFunction":
+        if _fn is None:
+            _fn = _make_function()
+        return _fn
+    raise AttributeError(name)
+
+
+def ldc_attention(q, k, v, c, g, doc_ids, window: int = DEFAULT_WINDOW, scale: Optional[float] = None):
+    return __getattr__("LDCFunction").apply(q, k, v, c, g, doc_ids, window, scale)

@@ -1,0 +1,283 @@
+// Device-side building blocks of the Lightweight DC kernels for gfx950 (CDNA4).
+//
+// Fragment conventions (verified on gfx950 for v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x4_f32; lane l, group g = l/16, column n = l%16):
+//   A operand   lane holds A[m = n][k-slots of group g]
+//   B operand   lane holds B[k-slots of group g][n]
+//   accumulator lane holds D[4g + i][n], i = 0..3
+// bf16: group g owns k-slots 8g..8g+7; fp32: group g owns the single slot g.
+//
+// ds_read_tr16_b64 (gfx950 LDS transpose read), per 16-lane group: lane
+// 4r+b supplies the address of 4 consecutive 16-bit elements; lane q
+// receives element q%4 of the addresses supplied by lanes 4e + q/4, e = 0..3.
+// Rows of a token-major LDS tile therefore land as the k-slots of an MFMA
+// operand whose m index runs along the head dimension.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace ldc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // storage of one bfloat16
+
+constexpr int kWave = 64;
+constexpr int kKeyBlocks = 8;                 // 16-token blocks in one wave's band
+constexpr int kBand = 16 * kKeyBlocks;        // 128 tokens
+constexpr int kHalo = kBand - 16;             // 112 rows before a 16-row block
+constexpr int kMaxWindow = kHalo + 1;         // 113: widest window the band holds
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<bf16_t> {
+  static constexpr bool bf16 = true;
+  static constexpr int pad = 8;  // LDS row padding in elements (16 bytes)
+};
+template <>
+struct Elem<float> {
+  static constexpr bool bf16 = false;
+  static constexpr int pad = 4;  // 16 bytes
+};
+
+// LDS row stride (elements) of a token-major tile with head dim D.
+template <typename T, int D>
+constexpr int lds_stride() { return D + Elem<T>::pad; }
+
+// Number of 32-bit registers the lane needs for one row's d-slice.
+template <typename T, int D>
+struct RowFrag {
+  // bf16: D/32 chunks of 8 values; fp32: D/4 values (one per 16x16x4 step)
+  static constexpr int n = Elem<T>::bf16 ? D / 32 : D / 4;
+  typename std::conditional<Elem<T>::bf16, bf16x8, float>::type v[n];
+};
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max4(float x) {
+  // reduce over the four 16-lane groups (lanes n, n+16, n+32, n+48)
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum4(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float b0, float b1,
+                                        float b2, float b3) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)b0; r[5] = (__bf16)b1; r[6] = (__bf16)b2; r[7] = (__bf16)b3;
+  return r;
+}
+
+// The d-slice of one token row that lane group g contributes to a contraction
+// over the head dimension (global memory source, zero when !valid).
+// bf16: chunk kk holds d = 32kk + 8g .. +7.  fp32: slot kk holds d = g*D/4 + kk.
+template <typename T, int D>
+__device__ __forceinline__ void load_row_frag(RowFrag<T, D>& f, const T* __restrict__ row, int g,
+                                              bool valid) {
+  if constexpr (Elem<T>::bf16) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      uint4 u = valid ? *reinterpret_cast<const uint4*>(row + 32 * kk + 8 * g) : uint4{0, 0, 0, 0};
+      f.v[kk] = __builtin_bit_cast(bf16x8, u);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < D / 4; kk += 4) {
+      float4 u = valid ? *reinterpret_cast<const float4*>(row + g * (D / 4) + kk)
+                       : float4{0.f, 0.f, 0.f, 0.f};
+      f.v[kk] = u.x; f.v[kk + 1] = u.y; f.v[kk + 2] = u.z; f.v[kk + 3] = u.w;
+    }
+  }
+}
+
+// acc += A x B for a contraction over the head dimension, where the A operand
+// row (m = this lane's n) is the LDS token row `lrow` and B is the fragment f.
+template <typename T, int D>
+__device__ __forceinline__ f32x4 mma_dcontract(f32x4 acc, const T* lrow, const RowFrag<T, D>& f,
+                                               int g) {
+  if constexpr (Elem<T>::bf16) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      uint4 u = *reinterpret_cast<const uint4*>(lrow + 32 * kk + 8 * g);
+      acc = mma(__builtin_bit_cast(bf16x8, u), f.v[kk], acc);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < D / 4; kk += 4) {
+      float4 u = *reinterpret_cast<const float4*>(lrow + g * (D / 4) + kk);
+      acc = mma(u.x, f.v[kk], acc);
+      acc = mma(u.y, f.v[kk + 1], acc);
+      acc = mma(u.z, f.v[kk + 2], acc);
+      acc = mma(u.w, f.v[kk + 3], acc);
+    }
+  }
+  return acc;
+}
+
+// Token-contraction operand: a 16 x 128 band held in accumulator layout
+// (lane: token rows 4g+i of block b, column n) packed as B-operand k-chunks.
+// bf16: chunk ks covers blocks 2ks, 2ks+1; slot j <-> block 2ks + j/4, row 4g + j%4.
+// The fp32 band is carried as two bf16 operands, hi = bf16(x) and
+// lo = bf16(x - hi), so the contraction keeps ~16 mantissa bits of x; the
+// other operand (a bf16 input tensor) is exact.
+template <typename T>
+struct BandOperand;
+template <>
+struct BandOperand<bf16_t> {
+  bf16x8 hi[kKeyBlocks / 2], lo[kKeyBlocks / 2];
+  __device__ __forceinline__ void set(const f32x4 (&p)[kKeyBlocks]) {
+#pragma unroll
+    for (int ks = 0; ks < kKeyBlocks / 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = p[2 * ks + (j >> 2)][j & 3];
+        const __bf16 h = (__bf16)x;
+        hi[ks][j] = h;
+        lo[ks][j] = (__bf16)(x - (float)h);
+      }
+  }
+};
+template <>
+struct BandOperand<float> {
+  f32x4 v[kKeyBlocks];
+  __device__ __forceinline__ void set(const f32x4 (&p)[kKeyBlocks]) {
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) v[b] = p[b];
+  }
+};
+
+// Contraction over the 128 band tokens:  out[d, n] = sum_tok X[tok, d] * P[tok, n]
+// with X a token-major LDS tile (rows base_row + tok) and P the band operand.
+// Result layout (lane: column n; register r = 4*blk + i):
+//   bf16: acc[2p+e][i] <-> d = 32p + 8g + 4e + i  (8 consecutive d per p)
+//   fp32: acc[db][i]   <-> d = 16db + 4g + i
+// `live` bit b set when token block b holds any admitted pair for this wave.
+template <typename T, int D>
+__device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* lds, int base_row,
+                                              const BandOperand<T>& P, uint32_t live, int g,
+                                              int n) {
+  constexpr int S = lds_stride<T, D>();
+#pragma unroll
+  for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
+  if constexpr (Elem<T>::bf16) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+    const int rr = n >> 2, bq = n & 3;
+#pragma unroll
+    for (int ks = 0; ks < kKeyBlocks / 2; ++ks) {
+      if (!((live >> (2 * ks)) & 3u)) continue;
+      const int row1 = base_row + 32 * ks + 4 * g + rr;
+#pragma unroll
+      for (int p = 0; p < D / 32; ++p) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int col = 32 * p + 8 * bq + 4 * e;
+          const bf16_t* a1 = lds + row1 * S + col;
+          const bf16_t* a2 = a1 + 16 * S;
+          bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
+          bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a2));
+          bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[2 * p + e] = mma(a, P.hi[ks], acc[2 * p + e]);
+          acc[2 * p + e] = mma(a, P.lo[ks], acc[2 * p + e]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      if (!((live >> b) & 1u)) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float* rowp = lds + (base_row + 16 * b + 4 * g + i) * S;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) acc[db] = mma(rowp[16 * db + n], P.v[b][i], acc[db]);
+      }
+    }
+  }
+}
+
+// Offset (elements) of the 4 consecutive d-values a lane holds in acc[r] of
+// mma_tcontract's result (the lane's group g).
+template <typename T>
+__device__ __forceinline__ int tcontract_d(int r, int g) {
+  if constexpr (Elem<T>::bf16)
+    return 32 * (r >> 1) + 8 * g + 4 * (r & 1);
+  else
+    return 16 * r + 4 * g;
+}
+
+__device__ __forceinline__ void store4(float* dst, f32x4 v, float s) {
+  *reinterpret_cast<float4*>(dst) = float4{v[0] * s, v[1] * s, v[2] * s, v[3] * s};
+}
+
+// Store a tcontract result row (scaled by s) to a float32 row.
+template <typename T, int D>
+__device__ __forceinline__ void store_row_f32(float* __restrict__ row, const f32x4 (&acc)[D / 16],
+                                              float s, int g) {
+#pragma unroll
+  for (int r = 0; r < D / 16; ++r) store4(row + tcontract_d<T>(r, g), acc[r], s);
+}
+
+// Stage `R` token rows [row0, row0+R) of head h of a [T,H,D] tensor into a
+// token-major LDS tile; rows outside [0, T) are zero-filled.
+template <typename T, int D, int R, int NT>
+__device__ __forceinline__ void stage_rows(T* lds, const T* __restrict__ src, int row0, int T_,
+                                           int H, int h) {
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;         // chunks per row
+  constexpr int TOTAL = R * CPR;
+  constexpr int IT = (TOTAL + NT - 1) / NT;
+  constexpr int BATCH = 4;             // loads in flight per thread
+  constexpr int S = lds_stride<T, D>();
+#pragma unroll
+  for (int it0 = 0; it0 < IT; it0 += BATCH) {
+    uint4 buf[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int idx = threadIdx.x + (it0 + u) * NT;
+      const int r = idx / CPR, ch = idx % CPR;
+      const int s = row0 + r;
+      buf[u] = uint4{0, 0, 0, 0};
+      if (it0 + u < IT && idx < TOTAL && s >= 0 && s < T_)
+        buf[u] = *reinterpret_cast<const uint4*>(src + ((size_t)s * H + h) * D + ch * EPC);
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int idx = threadIdx.x + (it0 + u) * NT;
+      const int r = idx / CPR, ch = idx % CPR;
+      if (it0 + u < IT && idx < TOTAL) *reinterpret_cast<uint4*>(lds + r * S + ch * EPC) = buf[u];
+    }
+  }
+}
+
+// Workgroup -> tile map that gives each XCD a contiguous run of tiles, so the
+// halo rows a tile shares with its neighbour are fetched through the same L2.
+// (Workgroups are dispatched to the 8 XCDs round-robin by block index.)
+__device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
+  constexpr int X = 8;
+  const int xcd = bid % X, idx = bid / X;
+  const int q = nblocks / X, rem = nblocks % X;
+  return xcd * q + (xcd < rem ? xcd : rem) + idx;
+}
+
+}  // namespace ldc

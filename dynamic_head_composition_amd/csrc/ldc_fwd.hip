@@ -1,0 +1,153 @@
+// Lightweight DC forward pass for gfx950.
+//
+// Computation (AITNT page "一个国产AI小透明，连续两次刷新NanoGPT Speedrun世界纪录",
+// section "第二刀-砍层内", Lightweight DC paragraph): per head a causal softmax
+// over a short local window, the heads' maps composed after the softmax into
+// one shared map, and the shared map applied to every head's values with a
+// per-head scale.
+//
+// Work split: one workgroup of NW waves owns BQ = 16*NW consecutive queries;
+// wave w owns 16 of them and the 128-token key band [q-112, q+16) that covers
+// their windows.  The workgroup stages the key span [q0-112, q0+BQ) of one
+// head at a time in LDS (K for the score pass, then V for the value pass).
+//
+// Scores are computed transposed, S^T = K Q^T, so each lane owns one query
+// column and 32 of its band entries: the softmax row reductions are in-lane
+// plus two cross-lane steps, and the composed map Pbar^T stays in registers
+// where it is directly the B operand of O^T = V^T Pbar^T (V^T read with LDS
+// transpose loads).  Pbar never leaves registers.
+#include "ldc_device.hpp"
+#include "ldc_internal.h"
+
+namespace ldc {
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
+  constexpr int BQ = 16 * NW;
+  constexpr int R = BQ + kHalo;
+  constexpr int NT = NW * kWave;
+  constexpr int S = lds_stride<T, D>();
+  __shared__ __attribute__((aligned(16))) T s_x[R * S];
+  __shared__ int s_doc[R];
+
+  const T* __restrict__ q = static_cast<const T*>(a.q);
+  const T* __restrict__ k = static_cast<const T*>(a.k);
+  const T* __restrict__ v = static_cast<const T*>(a.v);
+  float* __restrict__ o = a.o;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int q0 = tile * BQ;
+  const int span0 = q0 - kHalo;  // token of LDS row 0
+  const int brow = 16 * w;       // LDS row of this wave's band start (token qw - 112)
+  const int t = q0 + 16 * w + n; // this lane's query
+  const bool tval = t < a.T;
+  const int H = a.H;
+
+  for (int r = threadIdx.x; r < R; r += NT) {
+    const int s = span0 + r;
+    s_doc[r] = (s >= 0 && s < a.T) ? a.doc[s] : 0;
+  }
+  __syncthreads();
+
+  // Admission mask of this lane's 32 band entries: bit 4b+i <-> key row brow+16b+4g+i.
+  uint32_t mbits = 0;
+  if (tval) {
+    const int dt = s_doc[brow + kHalo + n];
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = brow + 16 * b + 4 * g + i;
+        const int s = span0 + r;
+        const bool ok = s >= 0 && s <= t && t - s < a.window && s_doc[r] == dt;
+        mbits |= (ok ? 1u : 0u) << (4 * b + i);
+      }
+  }
+  uint32_t live = 0;  // wave-uniform: token blocks with any admitted entry
+#pragma unroll
+  for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
+
+  const float sl2 = a.scale * kLog2e;
+  f32x4 pb[kKeyBlocks];
+#pragma unroll
+  for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
+
+  // ---- pass 1: per-head scores, softmax, composition into Pbar^T ----
+  for (int h = 0; h < H; ++h) {
+    __syncthreads();
+    stage_rows<T, D, R, NT>(s_x, k, span0, a.T, H, h);
+    RowFrag<T, D> qf;
+    load_row_frag<T, D>(qf, q + ((size_t)t * H + h) * D, g, tval);
+    const float ch = tval ? a.c[(size_t)t * H + h] : 0.f;
+    __syncthreads();
+
+    f32x4 sc[kKeyBlocks];
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      sc[b] = zero4();
+      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], s_x + (brow + 16 * b + n) * S, qf, g);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[b][i] *= sl2;
+        if ((mbits >> (4 * b + i)) & 1u) mx = fmaxf(mx, sc[b][i]);
+      }
+    mx = wave_max4(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(sc[b][i] - mx) : 0.f;
+        sc[b][i] = e;
+        sum += e;
+      }
+    sum = wave_sum4(sum);
+    const float coef = sum > 0.f ? ch / sum : 0.f;
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[b][i] += coef * sc[b][i];
+  }
+
+  BandOperand<T> pop;
+  pop.set(pb);
+
+  // ---- pass 2: O^T_h = V_h^T Pbar^T, scaled by G ----
+  for (int h = 0; h < H; ++h) {
+    __syncthreads();
+    stage_rows<T, D, R, NT>(s_x, v, span0, a.T, H, h);
+    const float gh = tval ? a.g[(size_t)t * H + h] : 0.f;
+    __syncthreads();
+    f32x4 acc[D / 16];
+    mma_tcontract<T, D>(acc, s_x, brow, pop, live, g, n);
+    if (tval) store_row_f32<T, D>(o + ((size_t)t * H + h) * D, acc, gh, g);
+  }
+}
+
+template <typename T, int D, int NW>
+static hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
+  constexpr int BQ = 16 * NW;
+  const int nblk = (int)((a.T + BQ - 1) / BQ);
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW>), dim3(nblk), dim3(NW * kWave), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, hipStream_t st) {
+  if (dtype == 0) {
+    if (d == 128) return launch_fwd<bf16_t, 128, 8>(a, st);
+    if (d == 64) return launch_fwd<bf16_t, 64, 8>(a, st);
+  } else {
+    if (d == 128) return launch_fwd<float, 128, 4>(a, st);
+    if (d == 64) return launch_fwd<float, 64, 4>(a, st);
+    if (d == 16) return launch_fwd<float, 16, 4>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ldc

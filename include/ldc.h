@@ -1,0 +1,103 @@
+/*
+ * ldc.h — C ABI of the Lightweight DC (LDC) attention layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer (AITNT page "一个国产AI小透明，连续两次刷新NanoGPT Speedrun世界纪录",
+ * section "第二刀-砍层内", Lightweight DC paragraph) reuses the attention
+ * block's Q and K, runs a per-head causal softmax over a local window of
+ * `window` tokens (112 in the GPT-2 small speedrun model), composes the heads'
+ * attention maps after the softmax into one shared map with per-token weights,
+ * and lets that shared map act on each head's Value through a per-head scale.
+ *
+ * With A(t) = { s : max(0, t-window+1) <= s <= t and doc_ids[s] == doc_ids[t] }:
+ *   S_h[t,s] = scale * <Q[t,h,:], K[s,h,:]>                 s in A(t)
+ *   P_h[t,:] = softmax over A(t) of S_h[t,:]
+ *   Pbar[t,s] = sum_h C[t,h] * P_h[t,s]          (C any real, not renormalised)
+ *   O[t,h,:] = G[t,h] * sum_{s in A(t)} Pbar[t,s] * V[s,h,:]
+ * The document cut and the use of query-indexed C and G are readings of the
+ * page, which leaves them open.
+ *
+ * Layout (all entry points): tokens are a flattened stream of T rows;
+ *   Q, K, V, dO, O, dQ, dK, dV : [T, H, d] row-major, element (t,h,j) at
+ *                                ((t*H)+h)*d + j;  Q, K, V, dO in the storage
+ *                                dtype, O and the gradients float32;
+ *   C, G, dC, dG               : [T, H] float32 row-major;
+ *   doc_ids                    : [T] int32, any values (only equality matters).
+ * Pointers are DEVICE pointers owned by the caller; base addresses must be
+ * 16-byte aligned.  Supported shapes: d in {64, 128} for LDC_BF16 and
+ * d in {16, 64, 128} for LDC_F32; 1 <= window <= 113; H >= 1; T >= 0
+ * (T == 0 is a no-op); T*H*d < 2^31.
+ *
+ * Execution: work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the call returns without synchronising.  The library allocates
+ * nothing, keeps no global state and is reentrant.  Outputs are fully
+ * overwritten (no accumulate mode).
+ *
+ * Errors: arguments are validated before any HIP call; a validation failure
+ * returns a non-zero ldc_status and has no side effects.  A failed kernel
+ * launch returns LDC_ERR_HIP.  Faults during execution surface at the caller's
+ * next synchronisation.
+ */
+#ifndef LDC_H_
+#define LDC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LDC_OK = 0,
+  LDC_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  LDC_ERR_SHAPE = 2,       /* T < 0, H < 1, window out of range, overflow   */
+  LDC_ERR_DTYPE = 3,       /* dtype is not an ldc_dtype value               */
+  LDC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned              */
+  LDC_ERR_UNSUPPORTED = 5, /* head dim not instantiated for this dtype      */
+  LDC_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required    */
+  LDC_ERR_HIP = 7          /* a HIP launch failed                           */
+} ldc_status;
+
+typedef enum {
+  LDC_BF16 = 0, /* Q, K, V, dO stored as bfloat16; fp32 accumulation  */
+  LDC_F32 = 1   /* Q, K, V, dO stored as float32                      */
+} ldc_dtype;
+
+/* Forward pass: writes O[T,H,d] in float32.
+ * q, k, v: [T,H,d] in `dtype`; c, g: [T,H] float32; doc_ids: [T] int32.
+ * scale: the softmax scale (1/sqrt(d) for the textbook choice).
+ * O is float32 for both storage dtypes: a bf16 store alone would round
+ * outputs of magnitude above ~5 by more than 2e-2. */
+int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale,
+            const void* q, const void* k, const void* v,
+            const float* c, const float* g, const int32_t* doc_ids,
+            float* o, void* stream);
+
+/* Backward pass: given dO, writes every gradient of the forward above in
+ * float32: dq, dk, dv [T,H,d] and dc, dg [T,H].  Same inputs as ldc_fwd.
+ * workspace: device scratch of at least ldc_bwd_workspace_bytes(...) bytes
+ * (16-byte aligned), owned by the caller; its contents on entry do not matter
+ * and are undefined on return.  The pass is deterministic: equal inputs give
+ * bitwise-equal outputs. */
+int ldc_bwd(int dtype, int64_t T, int H, int d, int window, float scale,
+            const void* q, const void* k, const void* v,
+            const float* c, const float* g, const int32_t* doc_ids,
+            const void* dO,
+            float* dq, float* dk, float* dv, float* dc, float* dg,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace ldc_bwd needs for these sizes (0 for T == 0). */
+size_t ldc_bwd_workspace_bytes(int dtype, int64_t T, int H, int d, int window);
+
+/* Human-readable name of a status code (static storage). */
+const char* ldc_status_str(int status);
+
+/* ABI version: major*10000 + minor*100 + patch. */
+int ldc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LDC_H_ */

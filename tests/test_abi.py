@@ -1,0 +1,105 @@
+"""Host-side tests of the C ABI (no GPU needed: validation precedes any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dynamic_head_composition_amd as ldc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ldc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ldc.LIB_PATH), reason="libldc.so not built")
+
+A = 1 << 20  # a fake, 16-byte aligned address; never dereferenced by these tests
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(ldc_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ldc.load_library()
+    names = declared_functions()
+    assert names == ["ldc_bwd", "ldc_bwd_workspace_bytes", "ldc_fwd", "ldc_status_str", "ldc_version"]
+    for nm in names:
+        assert hasattr(lib, nm)
+    out = subprocess.run(["nm", "-D", "--defined-only", ldc.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (ldc_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert ldc.version() == 10000
+    for code in range(8):
+        assert ldc.status_str(code).startswith("LDC_")
+    assert "unknown" in ldc.status_str(99)
+
+
+def test_workspace_bytes():
+    assert ldc.workspace_bytes(ldc.LDC_BF16, 65536, 6, 128, 112) == 65536 * 6 * 8
+    assert ldc.workspace_bytes(ldc.LDC_BF16, 0, 6, 128, 112) == 0
+    assert ldc.workspace_bytes(ldc.LDC_BF16, 10, 6, 16, 112) == 0  # unsupported -> 0
+
+
+def fwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None):
+    lib = ldc.load_library()
+    p = ptrs or [A] * 7
+    return lib.ldc_fwd(dtype, T, H, d, window, 0.1, *p, None)
+
+
+def bwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, ws=A, ws_bytes=None):
+    lib = ldc.load_library()
+    p = ptrs or [A] * 12
+    if ws_bytes is None:
+        ws_bytes = ldc.workspace_bytes(dtype, T, H, d, window)
+    return lib.ldc_bwd(dtype, T, H, d, window, 0.1, *p, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("call", [fwd_call, bwd_call])
+def test_validation_errors(call):
+    assert call(dtype=2) == 3                      # LDC_ERR_DTYPE
+    assert call(T=-1) == 2                         # LDC_ERR_SHAPE
+    assert call(H=0) == 2
+    assert call(window=0) == 2
+    assert call(window=114) == 2
+    assert call(T=1 << 31) == 2                    # too many rows
+    assert call(d=32) == 5                         # LDC_ERR_UNSUPPORTED
+    assert call(dtype=ldc.LDC_BF16, d=16) == 5
+    nptr = 7 if call is fwd_call else 12
+    for i in range(nptr):
+        ptrs = [A] * nptr
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == 1                # LDC_ERR_NULL
+        ptrs[i] = A + 8
+        assert call(ptrs=ptrs) == 4                # LDC_ERR_ALIGN
+
+
+def test_bwd_workspace_errors():
+    assert bwd_call(ws=None) == 6
+    assert bwd_call(ws_bytes=100) == 6
+    assert bwd_call(ws=A + 4) == 4
+
+
+def test_empty_stream_is_a_noop():
+    # T == 0 returns before any HIP call, even with NULL pointers
+    lib = ldc.load_library()
+    assert lib.ldc_fwd(0, 0, 6, 128, 112, 0.1, *([None] * 7), None) == 0
+    assert lib.ldc_bwd(0, 0, 6, 128, 112, 0.1, *([None] * 12), None, 0, None) == 0
+
+
+def test_oracle_and_product_share_no_code():
+    pkg = os.path.join(ROOT, "dynamic_head_composition_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            text = open(os.path.join(ROOT, "oracle", f), encoding="utf-8").read()
+            assert "dynamic_head_composition_amd" not in text, f
