@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the Lightweight DC layer (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one forward pass and one backward pass of the layer over the whole
+synthetic token stream of the workload (inputs resident in HBM before timing):
+ldc_fwd, then ldc_bwd as its two kernels ldc_bwd_q and ldc_bwd_kv, each timed
+with HIP events on the stream it runs on.  Rank 0 prints one JSON line.
+
+The workload (default: the GPT-2 small layer, T=65536 flattened tokens, 6
+heads of dim 128, window 112, documents of geometric length with mean 1024)
+is seeded and synthetic; it stands in for the FineWeb token stream the
+speedrun trains on.  The CPU baseline times the fp64 oracle on the host cores
+over a bounded leading part of the same stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3
+METRIC = "LDC attention fwd+bwd tokens/s on 1 MI355X (GPT-2-small shape); % MFMA peak"
+KERNELS = ("ldc_fwd", "ldc_bwd_q", "ldc_bwd_kv")
+SOURCES = ("ldc_device.hpp", "ldc_fwd.hip", "ldc_bwd.hip", "ldc_internal.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def valid_pairs(doc: np.ndarray, window: int) -> int:
+    """(query, key) pairs admitted by the window and the document cut, for a
+    stream whose documents are contiguous runs."""
+    T = len(doc)
+    starts = np.ones(T, dtype=bool)
+    starts[1:] = doc[1:] != doc[:-1]
+    idx = np.arange(T)
+    first = np.maximum.accumulate(np.where(starts, idx, 0))
+    return int(np.minimum(idx - first + 1, window).sum())
+
+
+def algorithmic_bytes_per_token(H: int, d: int, elem: int) -> dict:
+    """Compulsory HBM bytes per token of each kernel: every input it must read
+    and every output it must write, once."""
+    row = H * d
+    ch = 4 * H  # one float per (token, head)
+    return {
+        # q, k, v in; c, g, doc in; o (fp32) out
+        "ldc_fwd": 3 * row * elem + 2 * ch + 4 + row * 4,
+        # q, k, v, dO in; c, g, doc in; dq out; dc, dg out; statistics out
+        "ldc_bwd_q": 4 * row * elem + 2 * ch + 4 + row * 4 + 2 * ch + 2 * ch,
+        # q, k, v, dO in; c, g, dc, statistics, doc in; dk, dv out
+        "ldc_bwd_kv": 4 * row * elem + 3 * ch + 2 * ch + 4 + 2 * row * 4,
+    }
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in SOURCES:
+        with open(os.path.join(ROOT, "dynamic_head_composition_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float, chunk: int = 8192):
+    """Time the fp64 oracle (forward + backward) on leading slices of the
+    stream until `budget_s` seconds of CPU work or the whole stream."""
+    from oracle import ldc_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.T and time.perf_counter() - t0 < budget_s:
+        lo, hi = done, min(w.T, done + chunk)
+        orc.forward_slice(w.q, w.k, w.v, w.c, w.g, w.doc, lo, hi, window=w.window, scale=w.scale)
+        orc.backward_slice(w.q, w.k, w.v, w.c, w.g, w.doc, w.do, lo, hi, window=w.window, scale=w.scale)
+        done = hi
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward over tokens [0, {done}) of the same stream, "
+                      f"in {chunk}-token slices with their window halo; {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload index (2 = GPT-2 small layer fwd+bwd)")
+    ap.add_argument("--tokens", type=int, default=None, help="truncate the stream (quick runs only)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dynamic_head_composition_amd as ldc
+    from dynamic_head_composition_amd import workloads as wl
+
+    ldc.load_library()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+
+    log(f"generating workload {args.config} ...")
+    w = wl.config_workload(args.config, T=args.tokens)
+    x = w.torch_inputs("cuda")
+    T, H, d = w.T, w.H, w.d
+    elem = 2 if w.dtype == "bf16" else 4
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o = torch.empty((T, H, d), **f32)
+    grads = (torch.empty((T, H, d), **f32), torch.empty((T, H, d), **f32),
+             torch.empty((T, H, d), **f32), torch.empty((T, H), **f32), torch.empty((T, H), **f32))
+    code = ldc.LDC_BF16 if w.dtype == "bf16" else ldc.LDC_F32
+    ws = torch.empty(max(16, ldc.workspace_bytes(code, T, H, d, w.window)), dtype=torch.uint8, device="cuda")
+    ins = (x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"])
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        ldc.fwd(*ins, window=w.window, scale=w.scale, out=o)
+        if evs:
+            evs[1].record()
+        ldc.bwd(*ins, x["do"], window=w.window, scale=w.scale, out=grads, workspace=ws, part="q")
+        if evs:
+            evs[2].record()
+        ldc.bwd(*ins, x["do"], window=w.window, scale=w.scale, out=grads, workspace=ws, part="kv")
+        if evs:
+            evs[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if not all(bool(torch.isfinite(t).all()) for t in (o,) + grads):
+        raise SystemExit("non-finite outputs")
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = {kname: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                 for j, kname in enumerate(KERNELS)}
+    pairs = valid_pairs(w.doc, w.window)
+    flops = {"ldc_fwd": 4.0 * H * d * pairs, "ldc_bwd_q": None, "ldc_bwd_kv": None}
+    total_flops = 14.0 * H * d * pairs
+    bpt = algorithmic_bytes_per_token(H, d, elem)
+    per_kernel = {}
+    for kname in KERNELS:
+        sec = kernel_ms[kname] * 1e-3
+        per_kernel[kname] = {"avg_us": round(kernel_ms[kname] * 1e3, 2),
+                             "alg_bytes_per_launch": bpt[kname] * T,
+                             "alg_GBps": round(bpt[kname] * T / sec / 1e9, 1)}
+    dominant = max(KERNELS, key=lambda kname: kernel_ms[kname])
+    dom_sec = kernel_ms[dominant] * 1e-3
+    achieved = bpt[dominant] * T / dom_sec / 1e9
+    traffic = measured_traffic(dominant, w.name)
+    value = T / (ms_per_step * 1e-3)
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    alg_tflops = total_flops / (ms_per_step * 1e-3) / 1e12
+    alg_bytes_step = sum(bpt[kn] for kn in KERNELS) * T
+    ceiling_tps = HBM_PEAK_GBPS * 1e9 / (alg_bytes_step / T)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "heads": H, "head_dim": d, "window": w.window,
+                   "recipe": w.recipe, "valid_pairs": pairs, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "mfma_peak_frac": round(alg_tflops / mfma_peak, 5),
+        "alg_TFLOPs": round(alg_tflops, 2),
+        "step_hbm_ceiling_tokens_per_s": round(ceiling_tps, 1),
+        "step_roofline_frac": round(value / ceiling_tps, 4),
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,8 +51,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.ldc_fwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 8
     lib.ldc_fwd.restype = i32
-    lib.ldc_bwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 12 + [vp, sz, vp]
-    lib.ldc_bwd.restype = i32
+    for nm in ("ldc_bwd", "ldc_bwd_q", "ldc_bwd_kv"):
+        getattr(lib, nm).argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 12 + [vp, sz, vp]
+        getattr(lib, nm).restype = i32
     lib.ldc_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
     lib.ldc_bwd_workspace_bytes.restype = sz
     lib.ldc_status_str.argtypes = [i32]
@@ -144,8 +145,9 @@ def fwd(q, k, v, c, g, doc_ids, window: int = DEFAULT_WINDOW, scale: Optional[fl
 
 
 def bwd(q, k, v, c, g, doc_ids, do, window: int = DEFAULT_WINDOW, scale: Optional[float] = None,
-        out=None, workspace=None, stream=None):
-    """(dQ, dK, dV, dC, dG), all float32."""
+        out=None, workspace=None, stream=None, part: str = "all"):
+    """(dQ, dK, dV, dC, dG), all float32.  part="q" or "kv" runs one of the
+    two backward kernels only (ldc_bwd_q / ldc_bwd_kv); "all" runs both."""
     torch = _torch()
     lib = load_library()
     T, H, d = _check(q, k, v, c, g, doc_ids, do)
@@ -159,14 +161,15 @@ def bwd(q, k, v, c, g, doc_ids, do, window: int = DEFAULT_WINDOW, scale: Optiona
     need = workspace_bytes(_dtype_code(q), T, H, d, window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = lib.ldc_bwd(_dtype_code(q), T, H, d, window, float(scale),
+    entry = {"all": lib.ldc_bwd, "q": lib.ldc_bwd_q, "kv": lib.ldc_bwd_kv}[part]
+    st = entry(_dtype_code(q), T, H, d, window, float(scale),
                      q.data_ptr(), k.data_ptr(), v.data_ptr(), c.data_ptr(), g.data_ptr(),
                      doc_ids.data_ptr(), do.data_ptr(),
                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dc.data_ptr(), dg.data_ptr(),
                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                      _stream(q, stream))
     if st != 0:
-        raise LDCError(st, "ldc_bwd")
+        raise LDCError(st, {"all": "ldc_bwd", "q": "ldc_bwd_q", "kv": "ldc_bwd_kv"}[part])
     return dq, dk, dv, dc, dg
 
 

@@ -70,10 +70,10 @@ int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale, const v
   return e == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
 
-int ldc_bwd(int dtype, int64_t T, int H, int d, int window, float scale, const void* q,
-            const void* k, const void* v, const float* c, const float* g, const int32_t* doc_ids,
-            const void* dO, float* dq, float* dk, float* dv, float* dc, float* dg, void* workspace,
-            size_t workspace_bytes, void* stream) {
+static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, float scale,
+                     const void* q, const void* k, const void* v, const float* c, const float* g,
+                     const int32_t* doc_ids, const void* dO, float* dq, float* dk, float* dv,
+                     float* dc, float* dg, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_common(dtype, T, H, d, window);
   if (st != LDC_OK) return st;
   if (T == 0) return LDC_OK;
@@ -87,8 +87,21 @@ int ldc_bwd(int dtype, int64_t T, int H, int d, int window, float scale, const v
   if (!aligned16(workspace)) return LDC_ERR_ALIGN;
   ldc::BwdArgs a{(int)T, H, window, scale, q, k, v, dO, c, g, doc_ids,
                  dq, dk, dv, dc, dg, static_cast<float2*>(workspace)};
-  hipError_t e = ldc::bwd_dispatch(dtype, d, a, static_cast<hipStream_t>(stream));
+  hipError_t e = ldc::bwd_dispatch(dtype, d, a, parts, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
+
+#define LDC_BWD_PARAMS                                                                          \
+  int dtype, int64_t T, int H, int d, int window, float scale, const void *q, const void *k,    \
+      const void *v, const float *c, const float *g, const int32_t *doc_ids, const void *dO,    \
+      float *dq, float *dk, float *dv, float *dc, float *dg, void *workspace,                   \
+      size_t workspace_bytes, void *stream
+#define LDC_BWD_ARGS                                                                           \
+  dtype, T, H, d, window, scale, q, k, v, c, g, doc_ids, dO, dq, dk, dv, dc, dg, workspace,   \
+      workspace_bytes, stream
+
+int ldc_bwd(LDC_BWD_PARAMS) { return bwd_parts(3, LDC_BWD_ARGS); }
+int ldc_bwd_q(LDC_BWD_PARAMS) { return bwd_parts(1, LDC_BWD_ARGS); }
+int ldc_bwd_kv(LDC_BWD_PARAMS) { return bwd_parts(2, LDC_BWD_ARGS); }
 
 }  // extern "C"

@@ -365,24 +365,29 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
 }
 
 template <typename T, int D, int NW>
-static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
+static hipError_t launch_bwd(const BwdArgs& a, int parts, hipStream_t st) {
   constexpr int B = 16 * NW;
   const int nblk = (int)((a.T + B - 1) / B);
-  hipLaunchKernelGGL((bwd_q_kernel<T, D, NW>), dim3(nblk), dim3(NW * kWave), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_kv_kernel<T, D, NW>), dim3(nblk), dim3(NW * kWave), 0, st, a);
-  return hipGetLastError();
+  if (parts & 1) {
+    hipLaunchKernelGGL((bwd_q_kernel<T, D, NW>), dim3(nblk), dim3(NW * kWave), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (parts & 2) {
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, NW>), dim3(nblk), dim3(NW * kWave), 0, st, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
-hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, hipStream_t st) {
+hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, int parts, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 128) return launch_bwd<bf16_t, 128, 8>(a, st);
-    if (d == 64) return launch_bwd<bf16_t, 64, 8>(a, st);
+    if (d == 128) return launch_bwd<bf16_t, 128, 8>(a, parts, st);
+    if (d == 64) return launch_bwd<bf16_t, 64, 8>(a, parts, st);
   } else {
-    if (d == 128) return launch_bwd<float, 128, 4>(a, st);
-    if (d == 64) return launch_bwd<float, 64, 4>(a, st);
-    if (d == 16) return launch_bwd<float, 16, 4>(a, st);
+    if (d == 128) return launch_bwd<float, 128, 4>(a, parts, st);
+    if (d == 64) return launch_bwd<float, 64, 4>(a, parts, st);
+    if (d == 16) return launch_bwd<float, 16, 4>(a, parts, st);
   }
   return hipErrorInvalidValue;
 }

@@ -26,6 +26,7 @@ struct BwdArgs {
 };
 
 hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, hipStream_t st);
-hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, hipStream_t st);
+// parts: bit 0 = query-side kernel, bit 1 = key-side kernel
+hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, int parts, hipStream_t st);
 
 }  // namespace ldc

@@ -87,6 +87,26 @@ int ldc_bwd(int dtype, int64_t T, int H, int d, int window, float scale,
             float* dq, float* dk, float* dv, float* dc, float* dg,
             void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two kernels of ldc_bwd, callable one at a time (for per-kernel timing).
+ * ldc_bwd is exactly ldc_bwd_q followed by ldc_bwd_kv with the same
+ * arguments on the same stream:
+ *   ldc_bwd_q  writes dq, dc, dg and the softmax statistics (workspace);
+ *   ldc_bwd_kv reads dc and the workspace and writes dk, dv.
+ * Arguments, validation and errors as for ldc_bwd; pointers the kernel does
+ * not touch are still validated. */
+int ldc_bwd_q(int dtype, int64_t T, int H, int d, int window, float scale,
+              const void* q, const void* k, const void* v,
+              const float* c, const float* g, const int32_t* doc_ids,
+              const void* dO,
+              float* dq, float* dk, float* dv, float* dc, float* dg,
+              void* workspace, size_t workspace_bytes, void* stream);
+int ldc_bwd_kv(int dtype, int64_t T, int H, int d, int window, float scale,
+               const void* q, const void* k, const void* v,
+               const float* c, const float* g, const int32_t* doc_ids,
+               const void* dO,
+               float* dq, float* dk, float* dv, float* dc, float* dg,
+               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace ldc_bwd needs for these sizes (0 for T == 0). */
 size_t ldc_bwd_workspace_bytes(int dtype, int64_t T, int H, int d, int window);
 

@@ -24,7 +24,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = ldc.load_library()
     names = declared_functions()
-    assert names == ["ldc_bwd", "ldc_bwd_workspace_bytes", "ldc_fwd", "ldc_status_str", "ldc_version"]
+    assert names == ["ldc_bwd", "ldc_bwd_kv", "ldc_bwd_q", "ldc_bwd_workspace_bytes", "ldc_fwd",
+                     "ldc_status_str", "ldc_version"]
     for nm in names:
         assert hasattr(lib, nm)
     out = subprocess.run(["nm", "-D", "--defined-only", ldc.LIB_PATH], capture_output=True, text=True).stdout
@@ -51,15 +52,24 @@ def fwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None):
     return lib.ldc_fwd(dtype, T, H, d, window, 0.1, *p, None)
 
 
-def bwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, ws=A, ws_bytes=None):
+def bwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, ws=A, ws_bytes=None,
+             entry="ldc_bwd"):
     lib = ldc.load_library()
     p = ptrs or [A] * 12
     if ws_bytes is None:
         ws_bytes = ldc.workspace_bytes(dtype, T, H, d, window)
-    return lib.ldc_bwd(dtype, T, H, d, window, 0.1, *p, ws, ws_bytes, None)
+    return getattr(lib, entry)(dtype, T, H, d, window, 0.1, *p, ws, ws_bytes, None)
 
 
-@pytest.mark.parametrize("call", [fwd_call, bwd_call])
+def bwd_q_call(**kw):
+    return bwd_call(entry="ldc_bwd_q", **kw)
+
+
+def bwd_kv_call(**kw):
+    return bwd_call(entry="ldc_bwd_kv", **kw)
+
+
+@pytest.mark.parametrize("call", [fwd_call, bwd_call, bwd_q_call, bwd_kv_call])
 def test_validation_errors(call):
     assert call(dtype=2) == 3                      # LDC_ERR_DTYPE
     assert call(T=-1) == 2                         # LDC_ERR_SHAPE
@@ -78,10 +88,11 @@ def test_validation_errors(call):
         assert call(ptrs=ptrs) == 4                # LDC_ERR_ALIGN
 
 
-def test_bwd_workspace_errors():
-    assert bwd_call(ws=None) == 6
-    assert bwd_call(ws_bytes=100) == 6
-    assert bwd_call(ws=A + 4) == 4
+@pytest.mark.parametrize("entry", ["ldc_bwd", "ldc_bwd_q", "ldc_bwd_kv"])
+def test_bwd_workspace_errors(entry):
+    assert bwd_call(ws=None, entry=entry) == 6
+    assert bwd_call(ws_bytes=100, entry=entry) == 6
+    assert bwd_call(ws=A + 4, entry=entry) == 4
 
 
 def test_empty_stream_is_a_noop():
