@@ -12,15 +12,18 @@
 // Two deterministic kernels, no atomics and no zero-fill:
 //  * bwd_q  (query-centric, like the forward): each wave owns 16 queries and
 //    computes their dQ, dC, dG, plus each head's softmax statistics, which it
-//    hands to the second kernel through the workspace.
+//    hands to the second kernel through the workspace.  Phases over the
+//    heads: K_h staged (P_h, Pbar), V_h staged (dPbar, dG), K_h staged
+//    (P_h again, dC, dS, dQ).
 //  * bwd_kv (key-centric): each wave owns 16 keys and the 128 queries whose
-//    windows can hold them; it recomputes P_h from the statistics and makes
-//    three passes over the heads: Pbar (Q_h staged); dV_h and dPbar (dO_h
-//    staged); dS_h and dK_h (Q_h staged).
+//    windows can hold them; it recomputes P_h from the statistics.  Phases:
+//    Q_h staged (Pbar), dO_h staged (dV_h and dPbar), Q_h staged (dS_h, dK_h).
 // Neither writes a T x window map to HBM: the per-pair quantities live in
-// registers of the wave that needs them.
+// registers of the wave that needs them.  Tiles stream into LDS by DMA,
+// double-buffered, as in the forward pass.
 #include "ldc_device.hpp"
 #include "ldc_internal.h"
+#include "ldc_pipeline.hpp"
 
 namespace ldc {
 
@@ -33,8 +36,8 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   constexpr int BQ = 16 * NW;
   constexpr int R = BQ + kHalo;
   constexpr int NT = NW * kWave;
-  constexpr int S = lds_stride<T, D>();
-  __shared__ __attribute__((aligned(16))) T s_x[R * S];
+  __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
+  __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
   __shared__ int s_doc[R];
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
@@ -50,7 +53,20 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   const int brow = 16 * w;
   const int t = q0 + 16 * w + n;
   const bool tval = t < a.T;
+  const int tc = tval ? t : a.T - 1;
   const int H = a.H;
+  const int Hp = (H + 1) & ~1;
+
+  // phases: 0 = K (P_h, Pbar), 1 = V (dPbar, dG), 2 = K (dC, dS, dQ)
+  auto issue = [&](int phase, int h, bool on, auto bc) {
+    T* buf = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    issue_tile<T, D, R, NW>(buf, phase == 1 ? v : k, span0, a.T, H, h, on);
+  };
+  auto issue_next = [&](int phase, int j, auto bc) {
+    const NextStage ns = next_stage(phase, j, H, Hp, 3);
+    issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<1 - decltype(bc)::value>{});
+  };
+  issue(0, 0, true, Buf<0>{});
 
   for (int r = threadIdx.x; r < R; r += NT) {
     const int s = span0 + r;
@@ -58,7 +74,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   }
   __syncthreads();
   uint32_t mbits = 0;
-  if (tval) {
+  {
     const int dt = s_doc[brow + kHalo + n];
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
@@ -66,7 +82,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = brow + 16 * b + 4 * g + i;
         const int s = span0 + r;
-        const bool ok = s >= 0 && s <= t && t - s < a.window && s_doc[r] == dt;
+        const bool ok = tval & (s >= 0) & (s <= t) & (t - s < a.window) & (s_doc[r] == dt);
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
@@ -75,17 +91,14 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
 
   const float sl2 = a.scale * kLog2e;
-  f32x4 pb[kKeyBlocks], dpb[kKeyBlocks];
-#pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) pb[b] = dpb[b] = zero4();
 
-  // Scores of head h for this lane's query, softmax-normalised in place.
-  auto softmax_head = [&](f32x4 (&sc)[kKeyBlocks], const RowFrag<T, D>& qf, float& mx_out,
-                          float& inv_out) {
+  // Scores of head h for this lane's query from tile `cur`, softmax-normalised in place.
+  auto softmax_head = [&](f32x4 (&sc)[kKeyBlocks], const T* cur, const RowFrag<T, D>& qf,
+                          float& mx_out, float& inv_out) {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       sc[b] = zero4();
-      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], s_x + (brow + 16 * b + n) * S, qf, g);
+      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], cur, brow + 16 * b + n, qf, g);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -115,37 +128,51 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     inv_out = inv;
   };
 
-  // ---- phase A: P_h, Pbar, softmax statistics ----
-  for (int h = 0; h < H; ++h) {
-    __syncthreads();
-    stage_rows<T, D, R, NT>(s_x, k, span0, a.T, H, h);
+  // ---- phase 0: P_h, Pbar, softmax statistics ----
+  f32x4 pb[kKeyBlocks];
+#pragma unroll
+  for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
+  for_stage_pairs(Hp, [&](int j, auto bc) {
+    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    wait_dma();
+    const bool real = j < H;
+    const int hh = real ? j : 0;
     RowFrag<T, D> qf;
-    load_row_frag<T, D>(qf, q + ((size_t)t * H + h) * D, g, tval);
-    const float ch = tval ? a.c[(size_t)t * H + h] : 0.f;
-    __syncthreads();
+    load_row_frag<T, D>(qf, q + ((size_t)tc * H + hh) * D, g);
+    const float ch = a.c[(size_t)tc * H + hh];
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next(0, j, bc);
+    if (!real) return;
     f32x4 sc[kKeyBlocks];
     float mx, inv;
-    softmax_head(sc, qf, mx, inv);
-    if (tval && g == 0) a.stats[(size_t)t * H + h] = float2{mx, inv};
+    softmax_head(sc, cur, qf, mx, inv);
+    if (tval && g == 0) a.stats[(size_t)t * H + j] = float2{mx, inv};
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[b][i] += ch * sc[b][i];
-  }
+  });
 
-  // ---- phase B: B_h = dO_h V_h^T, dPbar, dG ----
-  for (int h = 0; h < H; ++h) {
-    __syncthreads();
-    stage_rows<T, D, R, NT>(s_x, v, span0, a.T, H, h);
+  // ---- phase 1: B_h = dO_h V_h^T, dPbar, dG ----
+  f32x4 dpb[kKeyBlocks];
+#pragma unroll
+  for (int b = 0; b < kKeyBlocks; ++b) dpb[b] = zero4();
+  for_stage_pairs(Hp, [&](int j, auto bc) {
+    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    wait_dma();
+    const bool real = j < H;
+    const int hh = real ? j : 0;
     RowFrag<T, D> df;
-    load_row_frag<T, D>(df, dO + ((size_t)t * H + h) * D, g, tval);
-    const float gh = tval ? a.g[(size_t)t * H + h] : 0.f;
-    __syncthreads();
+    load_row_frag<T, D>(df, dO + ((size_t)tc * H + hh) * D, g);
+    const float gh = a.g[(size_t)tc * H + hh];
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next(1, j, bc);
+    if (!real) return;
     float dgs = 0.f;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       if (!((live >> b) & 1u)) continue;
-      f32x4 bt = mma_dcontract<T, D>(zero4(), s_x + (brow + 16 * b + n) * S, df, g);
+      const f32x4 bt = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b + n, df, g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // masked entries of pb are exactly 0; bt there is finite (zero-filled rows)
@@ -154,27 +181,31 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
       }
     }
     dgs = wave_sum4(dgs);
-    if (tval && g == 0) a.dg[(size_t)t * H + h] = dgs;
-  }
+    if (tval && g == 0) a.dg[(size_t)t * H + j] = dgs;
+  });
 
-  // ---- phase C: recompute P_h, dC, dS, dQ ----
-  for (int h = 0; h < H; ++h) {
-    __syncthreads();
-    stage_rows<T, D, R, NT>(s_x, k, span0, a.T, H, h);
+  // ---- phase 2: recompute P_h, dC, dS, dQ ----
+  for_stage_pairs(Hp, [&](int j, auto bc) {
+    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    wait_dma();
+    const bool real = j < H;
+    const int hh = real ? j : 0;
     RowFrag<T, D> qf;
-    load_row_frag<T, D>(qf, q + ((size_t)t * H + h) * D, g, tval);
-    const float ch = tval ? a.c[(size_t)t * H + h] : 0.f;
-    __syncthreads();
+    load_row_frag<T, D>(qf, q + ((size_t)tc * H + hh) * D, g);
+    const float ch = a.c[(size_t)tc * H + hh];
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next(2, j, bc);
+    if (!real) return;
     f32x4 sc[kKeyBlocks];
     float mx, inv;
-    softmax_head(sc, qf, mx, inv);
+    softmax_head(sc, cur, qf, mx, inv);
     float dcs = 0.f;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dcs += sc[b][i] * dpb[b][i];
     dcs = wave_sum4(dcs);
-    if (tval && g == 0) a.dc[(size_t)t * H + h] = dcs;
+    if (tval && g == 0) a.dc[(size_t)t * H + j] = dcs;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
@@ -182,9 +213,10 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     BandOperand<T> dso;
     dso.set(sc);
     f32x4 acc[D / 16];
-    mma_tcontract<T, D>(acc, s_x, brow, dso, live, g, n);
-    if (tval) store_row_f32<T, D>(a.dq + ((size_t)t * H + h) * D, acc, a.scale, g);
-  }
+    mma_tcontract<T, D>(acc, cur, brow, dso, live, g, n);
+    if (tval) store_row_f32<T, D>(a.dq + ((size_t)t * H + j) * D, acc, a.scale, g);
+  });
+  wait_dma();
 }
 
 // ---------------------------------------------------------------------------
@@ -196,20 +228,21 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   constexpr int BK = 16 * NW;
   constexpr int R = BK + kHalo;  // query rows [k0, k0 + BK + 112)
+  constexpr int RP = (R + 63) / 64 * 64;
   constexpr int NT = NW * kWave;
-  constexpr int S = lds_stride<T, D>();
-  __shared__ __attribute__((aligned(16))) T s_x[R * S];
+  // per-row scalars of the staged head: C, G, dC, row max, 1/row sum
+  enum { SC_C = 0, SC_G = 1, SC_DC = 2, SC_MX = 3, SC_INV = 4, NSC = 5 };
+  __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
+  __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
+  __shared__ __attribute__((aligned(16))) float s_sc0[NSC * RP];
+  __shared__ __attribute__((aligned(16))) float s_sc1[NSC * RP];
   __shared__ int s_doc[R];
-  __shared__ __attribute__((aligned(16))) float s_c[R];
-  __shared__ __attribute__((aligned(16))) float s_g[R];
-  __shared__ __attribute__((aligned(16))) float s_dc[R];
-  __shared__ __attribute__((aligned(16))) float s_mx[R];
-  __shared__ __attribute__((aligned(16))) float s_inv[R];
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
   const T* __restrict__ v = static_cast<const T*>(a.v);
   const T* __restrict__ dO = static_cast<const T*>(a.dO);
+  const float* __restrict__ stats = reinterpret_cast<const float*>(a.stats);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -219,7 +252,27 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   const int brow = 16 * w;        // LDS row of this wave's first query (token kw)
   const int s = k0 + 16 * w + n;  // this lane's key
   const bool sval = s < a.T;
+  const int sc_ = sval ? s : a.T - 1;
   const int H = a.H;
+  const int Hp = (H + 1) & ~1;
+
+  // phases: 0 = Q (Pbar), 1 = dO (dV, dPbar), 2 = Q (dS, dK)
+  auto issue = [&](int phase, int h, bool on, auto bc) {
+    constexpr int B = decltype(bc)::value;
+    T* buf = B == 0 ? s_x0 : s_x1;
+    float* sc = B == 0 ? s_sc0 : s_sc1;
+    issue_tile<T, D, R, NW>(buf, phase == 1 ? dO : q, span0, a.T, H, h, on);
+    issue_scalars<R, NW>(sc + SC_C * RP, a.c, 1, 0, span0, a.T, H, h, on);
+    issue_scalars<R, NW>(sc + SC_G * RP, a.g, 1, 0, span0, a.T, H, h, on);
+    issue_scalars<R, NW>(sc + SC_DC * RP, a.dc, 1, 0, span0, a.T, H, h, on);
+    issue_scalars<R, NW>(sc + SC_MX * RP, stats, 2, 0, span0, a.T, H, h, on);
+    issue_scalars<R, NW>(sc + SC_INV * RP, stats, 2, 1, span0, a.T, H, h, on);
+  };
+  auto issue_next = [&](int phase, int j, auto bc) {
+    const NextStage ns = next_stage(phase, j, H, Hp, 3);
+    issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<1 - decltype(bc)::value>{});
+  };
+  issue(0, 0, true, Buf<0>{});
 
   for (int r = threadIdx.x; r < R; r += NT) {
     const int t = span0 + r;
@@ -227,7 +280,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   }
   __syncthreads();
   uint32_t mbits = 0;  // bit 4b+i <-> query row brow + 16b + 4g + i
-  if (sval) {
+  {
     const int ds = s_doc[brow + n];
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
@@ -235,7 +288,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = brow + 16 * b + 4 * g + i;
         const int t = span0 + r;
-        const bool ok = t < a.T && t >= s && t - s < a.window && s_doc[r] == ds;
+        const bool ok = sval & (t < a.T) & (t >= s) & (t - s < a.window) & (s_doc[r] == ds);
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
@@ -243,125 +296,117 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
 
-  auto stage_scalars = [&](int h) {
-    for (int r = threadIdx.x; r < R; r += NT) {
-      const int t = span0 + r;
-      float c = 0.f, gg = 0.f, dc = 0.f, mx = 0.f, inv = 0.f;
-      if (t < a.T) {
-        const size_t i = (size_t)t * H + h;
-        c = a.c[i];
-        gg = a.g[i];
-        dc = a.dc[i];
-        const float2 st = a.stats[i];
-        mx = st.x;
-        inv = st.y;
-      }
-      s_c[r] = c;
-      s_g[r] = gg;
-      s_dc[r] = dc;
-      s_mx[r] = mx;
-      s_inv[r] = inv;
-    }
+  auto rows4 = [&](const float* sc, int field, int b) {
+    return *reinterpret_cast<const float4*>(sc + field * RP + brow + 16 * b + 4 * g);
   };
-  auto rows4 = [&](const float* arr, int b) {
-    return *reinterpret_cast<const float4*>(arr + brow + 16 * b + 4 * g);
-  };
-
   const float sl2 = a.scale * kLog2e;
-  // P_h of head h on this lane's band (rows = queries), from the statistics.
-  auto probs = [&](f32x4 (&sc)[kKeyBlocks], const RowFrag<T, D>& kf) {
+  // P_h of the staged head on this lane's band (rows = queries), from the statistics.
+  auto probs = [&](f32x4 (&p)[kKeyBlocks], const T* cur, const float* sc, const RowFrag<T, D>& kf) {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
-      sc[b] = zero4();
-      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], s_x + (brow + 16 * b + n) * S, kf, g);
-      const float4 mx = rows4(s_mx, b), inv = rows4(s_inv, b);
+      p[b] = zero4();
+      if ((live >> b) & 1u) p[b] = mma_dcontract<T, D>(p[b], cur, brow + 16 * b + n, kf, g);
+      const float4 mx = rows4(sc, SC_MX, b), inv = rows4(sc, SC_INV, b);
       const float mxv[4] = {mx.x, mx.y, mx.z, mx.w}, invv[4] = {inv.x, inv.y, inv.z, inv.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sc[b][i] = ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(sc[b][i] * sl2 - mxv[i]) * invv[i] : 0.f;
+        p[b][i] = ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(p[b][i] * sl2 - mxv[i]) * invv[i] : 0.f;
     }
   };
 
-  // ---- pass 1: Pbar on the band (Q_h staged) ----
+  // ---- phase 0 (Q_h staged): Pbar on the band ----
   f32x4 pb[kKeyBlocks];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
-  for (int h = 0; h < H; ++h) {
-    __syncthreads();
-    stage_rows<T, D, R, NT>(s_x, q, span0, a.T, H, h);
-    stage_scalars(h);
+  for_stage_pairs(Hp, [&](int j, auto bc) {
+    constexpr int B = decltype(bc)::value;
+    const T* cur = B == 0 ? s_x0 : s_x1;
+    const float* sc = B == 0 ? s_sc0 : s_sc1;
+    wait_dma();
+    const bool real = j < H;
     RowFrag<T, D> kf;
-    load_row_frag<T, D>(kf, k + ((size_t)s * H + h) * D, g, sval);
-    __syncthreads();
-    f32x4 sc[kKeyBlocks];
-    probs(sc, kf);
+    load_row_frag<T, D>(kf, k + ((size_t)sc_ * H + (real ? j : 0)) * D, g);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next(0, j, bc);
+    if (!real) return;
+    f32x4 p[kKeyBlocks];
+    probs(p, cur, sc, kf);
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
-      const float4 c4 = rows4(s_c, b);
+      const float4 c4 = rows4(sc, SC_C, b);
       const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pb[b][i] += cv[i] * sc[b][i];
+      for (int i = 0; i < 4; ++i) pb[b][i] += cv[i] * p[b][i];
     }
-  }
+  });
 
-  // ---- pass 2 (dO_h staged): dV_h = (G_h o Pbar)^T dO_h, and dPbar ----
+  // ---- phase 1 (dO_h staged): dV_h = (G_h o Pbar)^T dO_h, and dPbar ----
   f32x4 dpb[kKeyBlocks];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) dpb[b] = zero4();
-  for (int h = 0; h < H; ++h) {
-    __syncthreads();
-    stage_rows<T, D, R, NT>(s_x, dO, span0, a.T, H, h);
-    stage_scalars(h);
+  for_stage_pairs(Hp, [&](int j, auto bc) {
+    constexpr int B = decltype(bc)::value;
+    const T* cur = B == 0 ? s_x0 : s_x1;
+    const float* sc = B == 0 ? s_sc0 : s_sc1;
+    wait_dma();
+    const bool real = j < H;
     RowFrag<T, D> vf;
-    load_row_frag<T, D>(vf, v + ((size_t)s * H + h) * D, g, sval);
-    __syncthreads();
+    load_row_frag<T, D>(vf, v + ((size_t)sc_ * H + (real ? j : 0)) * D, g);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next(1, j, bc);
+    if (!real) return;
     {
       f32x4 gp[kKeyBlocks];
 #pragma unroll
       for (int b = 0; b < kKeyBlocks; ++b) {
-        const float4 g4 = rows4(s_g, b);
+        const float4 g4 = rows4(sc, SC_G, b);
         gp[b] = f32x4{g4.x * pb[b][0], g4.y * pb[b][1], g4.z * pb[b][2], g4.w * pb[b][3]};
       }
       BandOperand<T> op;
       op.set(gp);
       f32x4 acc[D / 16];
-      mma_tcontract<T, D>(acc, s_x, brow, op, live, g, n);
-      if (sval) store_row_f32<T, D>(a.dv + ((size_t)s * H + h) * D, acc, 1.f, g);
+      mma_tcontract<T, D>(acc, cur, brow, op, live, g, n);
+      if (sval) store_row_f32<T, D>(a.dv + ((size_t)s * H + j) * D, acc, 1.f, g);
     }
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       if (!((live >> b) & 1u)) continue;
-      const f32x4 bt = mma_dcontract<T, D>(zero4(), s_x + (brow + 16 * b + n) * S, vf, g);
-      const float4 g4 = rows4(s_g, b);
+      const f32x4 bt = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b + n, vf, g);
+      const float4 g4 = rows4(sc, SC_G, b);
       const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) dpb[b][i] += gv[i] * bt[i];
     }
-  }
+  });
 
-  // ---- pass 3 (Q_h staged): P_h, dS_h, dK_h = scale dS_h^T Q_h ----
-  for (int h = 0; h < H; ++h) {
-    __syncthreads();
-    stage_rows<T, D, R, NT>(s_x, q, span0, a.T, H, h);
-    stage_scalars(h);
+  // ---- phase 2 (Q_h staged): P_h, dS_h, dK_h = scale dS_h^T Q_h ----
+  for_stage_pairs(Hp, [&](int j, auto bc) {
+    constexpr int B = decltype(bc)::value;
+    const T* cur = B == 0 ? s_x0 : s_x1;
+    const float* sc = B == 0 ? s_sc0 : s_sc1;
+    wait_dma();
+    const bool real = j < H;
     RowFrag<T, D> kf;
-    load_row_frag<T, D>(kf, k + ((size_t)s * H + h) * D, g, sval);
-    __syncthreads();
-    f32x4 sc[kKeyBlocks];
-    probs(sc, kf);
+    load_row_frag<T, D>(kf, k + ((size_t)sc_ * H + (real ? j : 0)) * D, g);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next(2, j, bc);
+    if (!real) return;
+    f32x4 p[kKeyBlocks];
+    probs(p, cur, sc, kf);
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
-      const float4 c4 = rows4(s_c, b), dc4 = rows4(s_dc, b);
+      const float4 c4 = rows4(sc, SC_C, b), dc4 = rows4(sc, SC_DC, b);
       const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, dcv[4] = {dc4.x, dc4.y, dc4.z, dc4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[b][i] = cv[i] * sc[b][i] * (dpb[b][i] - dcv[i]);
+      for (int i = 0; i < 4; ++i) p[b][i] = cv[i] * p[b][i] * (dpb[b][i] - dcv[i]);
     }
     BandOperand<T> dso;
-    dso.set(sc);
+    dso.set(p);
     f32x4 acc[D / 16];
-    mma_tcontract<T, D>(acc, s_x, brow, dso, live, g, n);
-    if (sval) store_row_f32<T, D>(a.dk + ((size_t)s * H + h) * D, acc, a.scale, g);
-  }
+    mma_tcontract<T, D>(acc, cur, brow, dso, live, g, n);
+    if (sval) store_row_f32<T, D>(a.dk + ((size_t)s * H + j) * D, acc, a.scale, g);
+  });
+  wait_dma();
 }
 
 template <typename T, int D, int NW>
@@ -385,7 +430,7 @@ hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, int parts, hipStream
     if (d == 128) return launch_bwd<bf16_t, 128, 8>(a, parts, st);
     if (d == 64) return launch_bwd<bf16_t, 64, 8>(a, parts, st);
   } else {
-    if (d == 128) return launch_bwd<float, 128, 4>(a, parts, st);
+    if (d == 128) return launch_bwd<float, 128, 2>(a, parts, st);
     if (d == 64) return launch_bwd<float, 64, 4>(a, parts, st);
     if (d == 16) return launch_bwd<float, 16, 4>(a, parts, st);
   }

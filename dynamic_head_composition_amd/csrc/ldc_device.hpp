@@ -12,6 +12,14 @@
 // receives element q%4 of the addresses supplied by lanes 4e + q/4, e = 0..3.
 // Rows of a token-major LDS tile therefore land as the k-slots of an MFMA
 // operand whose m index runs along the head dimension.
+//
+// buffer_load_dwordx4 ... lds (verified on gfx950): lane i's 16 bytes land at
+// LDS address M0 + 16*i; offsets outside the buffer's range read as zero.
+//
+// LDS tiles are token-major rows of D elements with no padding; the 16-byte
+// chunk c of row r is stored at chunk position c ^ swz(r).  The swizzle makes
+// both read patterns conflict-free: 16 consecutive rows at one chunk (score
+// operands) and 4 consecutive rows x 4 consecutive chunks (transpose reads).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,7 +32,9 @@ namespace ldc {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // storage of one bfloat16
+typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
 
 constexpr int kWave = 64;
 constexpr int kKeyBlocks = 8;                 // 16-token blocks in one wave's band
@@ -33,22 +43,45 @@ constexpr int kHalo = kBand - 16;             // 112 rows before a 16-row block
 constexpr int kMaxWindow = kHalo + 1;         // 113: widest window the band holds
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Direct global -> LDS load through a buffer resource (llvm.amdgcn.raw.buffer.load.lds).
+extern "C" __device__ void ldc_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
+                                               int soffset, int offset,
+                                               int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 template <typename T>
 struct Elem;
 template <>
 struct Elem<bf16_t> {
   static constexpr bool bf16 = true;
-  static constexpr int pad = 8;  // LDS row padding in elements (16 bytes)
 };
 template <>
 struct Elem<float> {
   static constexpr bool bf16 = false;
-  static constexpr int pad = 4;  // 16 bytes
 };
 
-// LDS row stride (elements) of a token-major tile with head dim D.
 template <typename T, int D>
-constexpr int lds_stride() { return D + Elem<T>::pad; }
+struct Tile {
+  static constexpr int row_bytes = D * (int)sizeof(T);
+  static constexpr int chunks = row_bytes / 16;      // 16-byte chunks per row
+  static constexpr int rows_per_inst = 64 / chunks;  // rows one wave-wide DMA fills
+  // chunk position of logical chunk c in row r
+  static __device__ __forceinline__ int pos(int r, int c) {
+    if constexpr (Elem<T>::bf16 && D == 128) {
+      return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    } else if constexpr (Elem<T>::bf16 && D == 64) {
+      return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    } else if constexpr (D == 16) {
+      return c ^ ((r >> 2) & 3);
+    } else {
+      return c ^ (r & 15);
+    }
+  }
+  // byte offset of element `col` (16-byte aligned group start) in row r
+  static __device__ __forceinline__ int off(int r, int col) {
+    constexpr int epc = 16 / (int)sizeof(T);
+    return r * row_bytes + pos(r, col / epc) * 16 + (col % epc) * (int)sizeof(T);
+  }
+};
 
 // Number of 32-bit registers the lane needs for one row's d-slice.
 template <typename T, int D>
@@ -89,43 +122,124 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// Buffer resources and DMA staging
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);  // stride 0
+  r[2] = (int)bytes;                            // num_records (bytes)
+  r[3] = 0x00020000;                            // gfx9 data format: 32-bit, raw
+  return r;
+}
+
+// Issue (asynchronously) the DMA of rows [row0, row0+R) of head h of a
+// [T,H,D] tensor into an LDS tile; rows outside [0,T) read as zero, and
+// nothing but zeros is read when !on.  Every wave issues the same number of
+// DMA instructions, unconditionally (a surplus instruction repeats the last
+// one: identical bytes to identical LDS addresses), so that the compiler's
+// wait counters see one straight-line sequence of vector-memory operations.
+// Completion is waited for with s_waitcnt vmcnt + a barrier by the caller.
+template <typename T, int D, int R, int NW>
+__device__ __forceinline__ void issue_tile(T* tile, const T* __restrict__ src, int row0, int T_,
+                                           int H, int h, bool on = true) {
+  using TL = Tile<T, D>;
+  constexpr int RPI = TL::rows_per_inst;
+  static_assert(R % RPI == 0, "tile rows must fill whole DMA instructions");
+  constexpr int NI = R / RPI;
+  constexpr int NIW = (NI + NW - 1) / NW;  // instructions per wave
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lo = row0 > 0 ? row0 : 0;
+  const int hi = (row0 + R < T_) ? row0 + R : T_;
+  const uint32_t rstride = (uint32_t)H * D * sizeof(T);
+  const uint32_t bytes =
+      (on && hi > lo) ? (uint32_t)(hi - 1 - lo) * rstride + (uint32_t)D * sizeof(T) : 0u;
+  const i32x4 rsrc = make_rsrc(src + ((size_t)(hi > lo ? lo : 0) * H + h) * D, bytes);
+  const int rsub = lane / TL::chunks, pc = lane % TL::chunks;
+  char* base = reinterpret_cast<char*>(tile);
+#pragma unroll
+  for (int u = 0; u < NIW; ++u) {
+    const int j = (w + u * NW < NI) ? w + u * NW : NI - 1;
+    const int rl = j * RPI + rsub;
+    const int s = row0 + rl;
+    const int lc = TL::pos(rl, pc);  // the swizzle is an involution: pos(pos(c)) = c
+    const uint32_t voff = (s >= lo && s < hi) ? (uint32_t)(s - lo) * rstride + (uint32_t)lc * 16u : bytes;
+    ldc_buffer_load_lds(rsrc, (lds_u32_ptr)(base + j * 1024), 16, (int)voff, 0, 0, 0);
+  }
+}
+
+// Issue the DMA of the float scalars x[(t*H + h)*spt + fld] for rows
+// [row0, row0+R) into an LDS array of round_up(R, 64) floats; rows outside
+// [0,T) (or everything when !on) read as zero.  Same issue discipline as
+// issue_tile.
+template <int R, int NW>
+__device__ __forceinline__ void issue_scalars(float* arr, const float* __restrict__ src, int spt,
+                                              int fld, int row0, int T_, int H, int h,
+                                              bool on = true) {
+  constexpr int NI = (R + 63) / 64;
+  constexpr int NIW = (NI + NW - 1) / NW;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lo = row0 > 0 ? row0 : 0;
+  const int hi = (row0 + R < T_) ? row0 + R : T_;
+  const uint32_t rstride = (uint32_t)H * spt * 4u;
+  const uint32_t bytes = (on && hi > lo) ? (uint32_t)(hi - 1 - lo) * rstride + 4u : 0u;
+  const i32x4 rsrc = make_rsrc(src + ((size_t)(hi > lo ? lo : 0) * H + h) * spt + fld, bytes);
+  char* base = reinterpret_cast<char*>(arr);
+#pragma unroll
+  for (int u = 0; u < NIW; ++u) {
+    const int j = (w + u * NW < NI) ? w + u * NW : NI - 1;
+    const int s = row0 + j * 64 + lane;
+    const uint32_t voff = (s >= lo && s < hi) ? (uint32_t)(s - lo) * rstride : bytes;
+    ldc_buffer_load_lds(rsrc, (lds_u32_ptr)(base + j * 256), 4, (int)voff, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_dma() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// MFMA building blocks over staged tiles
+// ---------------------------------------------------------------------------
 // The d-slice of one token row that lane group g contributes to a contraction
-// over the head dimension (global memory source, zero when !valid).
+// over the head dimension (global memory source; the caller passes a valid
+// row and ignores the result of lanes it does not need).
 // bf16: chunk kk holds d = 32kk + 8g .. +7.  fp32: slot kk holds d = g*D/4 + kk.
 template <typename T, int D>
-__device__ __forceinline__ void load_row_frag(RowFrag<T, D>& f, const T* __restrict__ row, int g,
-                                              bool valid) {
+__device__ __forceinline__ void load_row_frag(RowFrag<T, D>& f, const T* __restrict__ row, int g) {
   if constexpr (Elem<T>::bf16) {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      uint4 u = valid ? *reinterpret_cast<const uint4*>(row + 32 * kk + 8 * g) : uint4{0, 0, 0, 0};
-      f.v[kk] = __builtin_bit_cast(bf16x8, u);
-    }
+    for (int kk = 0; kk < D / 32; ++kk)
+      f.v[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + 32 * kk + 8 * g));
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 4; kk += 4) {
-      float4 u = valid ? *reinterpret_cast<const float4*>(row + g * (D / 4) + kk)
-                       : float4{0.f, 0.f, 0.f, 0.f};
+      const float4 u = *reinterpret_cast<const float4*>(row + g * (D / 4) + kk);
       f.v[kk] = u.x; f.v[kk + 1] = u.y; f.v[kk + 2] = u.z; f.v[kk + 3] = u.w;
     }
   }
 }
 
 // acc += A x B for a contraction over the head dimension, where the A operand
-// row (m = this lane's n) is the LDS token row `lrow` and B is the fragment f.
+// row (m = this lane's n) is tile row `r` and B is the fragment f.
 template <typename T, int D>
-__device__ __forceinline__ f32x4 mma_dcontract(f32x4 acc, const T* lrow, const RowFrag<T, D>& f,
-                                               int g) {
+__device__ __forceinline__ f32x4 mma_dcontract(f32x4 acc, const T* tile, int r,
+                                               const RowFrag<T, D>& f, int g) {
+  using TL = Tile<T, D>;
+  const char* base = reinterpret_cast<const char*>(tile);
   if constexpr (Elem<T>::bf16) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      uint4 u = *reinterpret_cast<const uint4*>(lrow + 32 * kk + 8 * g);
+      uint4 u = *reinterpret_cast<const uint4*>(base + TL::off(r, 32 * kk + 8 * g));
       acc = mma(__builtin_bit_cast(bf16x8, u), f.v[kk], acc);
     }
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 4; kk += 4) {
-      float4 u = *reinterpret_cast<const float4*>(lrow + g * (D / 4) + kk);
+      float4 u = *reinterpret_cast<const float4*>(base + TL::off(r, g * (D / 4) + kk));
       acc = mma(u.x, f.v[kk], acc);
       acc = mma(u.y, f.v[kk + 1], acc);
       acc = mma(u.z, f.v[kk + 2], acc);
@@ -168,16 +282,17 @@ struct BandOperand<float> {
 };
 
 // Contraction over the 128 band tokens:  out[d, n] = sum_tok X[tok, d] * P[tok, n]
-// with X a token-major LDS tile (rows base_row + tok) and P the band operand.
+// with X a staged tile (rows base_row + tok) and P the band operand.
 // Result layout (lane: column n; register r = 4*blk + i):
 //   bf16: acc[2p+e][i] <-> d = 32p + 8g + 4e + i  (8 consecutive d per p)
 //   fp32: acc[db][i]   <-> d = 16db + 4g + i
 // `live` bit b set when token block b holds any admitted pair for this wave.
 template <typename T, int D>
-__device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* lds, int base_row,
+__device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* tile, int base_row,
                                               const BandOperand<T>& P, uint32_t live, int g,
                                               int n) {
-  constexpr int S = lds_stride<T, D>();
+  using TL = Tile<T, D>;
+  const char* base = reinterpret_cast<const char*>(tile);
 #pragma unroll
   for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
   if constexpr (Elem<T>::bf16) {
@@ -186,14 +301,13 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* lds
 #pragma unroll
     for (int ks = 0; ks < kKeyBlocks / 2; ++ks) {
       if (!((live >> (2 * ks)) & 3u)) continue;
-      const int row1 = base_row + 32 * ks + 4 * g + rr;
+      const int row1 = base_row + 32 * ks + 4 * g + rr;  // row1 + 16 has the same swizzle
 #pragma unroll
       for (int p = 0; p < D / 32; ++p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int col = 32 * p + 8 * bq + 4 * e;
-          const bf16_t* a1 = lds + row1 * S + col;
-          const bf16_t* a2 = a1 + 16 * S;
+          const char* a1 = base + TL::off(row1, 32 * p + 8 * bq + 4 * e);
+          const char* a2 = a1 + 16 * TL::row_bytes;
           bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
           bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a2));
           bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -208,9 +322,12 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* lds
       if (!((live >> b) & 1u)) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float* rowp = lds + (base_row + 16 * b + 4 * g + i) * S;
+        const int r = base_row + 16 * b + 4 * g + i;
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) acc[db] = mma(rowp[16 * db + n], P.v[b][i], acc[db]);
+        for (int db = 0; db < D / 16; ++db) {
+          const float x = *reinterpret_cast<const float*>(base + TL::off(r, 16 * db + n));
+          acc[db] = mma(x, P.v[b][i], acc[db]);
+        }
       }
     }
   }
@@ -236,38 +353,6 @@ __device__ __forceinline__ void store_row_f32(float* __restrict__ row, const f32
                                               float s, int g) {
 #pragma unroll
   for (int r = 0; r < D / 16; ++r) store4(row + tcontract_d<T>(r, g), acc[r], s);
-}
-
-// Stage `R` token rows [row0, row0+R) of head h of a [T,H,D] tensor into a
-// token-major LDS tile; rows outside [0, T) are zero-filled.
-template <typename T, int D, int R, int NT>
-__device__ __forceinline__ void stage_rows(T* lds, const T* __restrict__ src, int row0, int T_,
-                                           int H, int h) {
-  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
-  constexpr int CPR = D / EPC;         // chunks per row
-  constexpr int TOTAL = R * CPR;
-  constexpr int IT = (TOTAL + NT - 1) / NT;
-  constexpr int BATCH = 4;             // loads in flight per thread
-  constexpr int S = lds_stride<T, D>();
-#pragma unroll
-  for (int it0 = 0; it0 < IT; it0 += BATCH) {
-    uint4 buf[BATCH];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int idx = threadIdx.x + (it0 + u) * NT;
-      const int r = idx / CPR, ch = idx % CPR;
-      const int s = row0 + r;
-      buf[u] = uint4{0, 0, 0, 0};
-      if (it0 + u < IT && idx < TOTAL && s >= 0 && s < T_)
-        buf[u] = *reinterpret_cast<const uint4*>(src + ((size_t)s * H + h) * D + ch * EPC);
-    }
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int idx = threadIdx.x + (it0 + u) * NT;
-      const int r = idx / CPR, ch = idx % CPR;
-      if (it0 + u < IT && idx < TOTAL) *reinterpret_cast<uint4*>(lds + r * S + ch * EPC) = buf[u];
-    }
-  }
 }
 
 // Workgroup -> tile map that gives each XCD a contiguous run of tiles, so the

@@ -8,8 +8,10 @@
 //
 // Work split: one workgroup of NW waves owns BQ = 16*NW consecutive queries;
 // wave w owns 16 of them and the 128-token key band [q-112, q+16) that covers
-// their windows.  The workgroup stages the key span [q0-112, q0+BQ) of one
-// head at a time in LDS (K for the score pass, then V for the value pass).
+// their windows.  The workgroup streams the key span [q0-112, q0+BQ) of one
+// head at a time into LDS by DMA, double-buffered: all heads' K (score
+// phase), then all heads' V (value phase); the next head's tile is in flight
+// while the current one is used.
 //
 // Scores are computed transposed, S^T = K Q^T, so each lane owns one query
 // column and 32 of its band entries: the softmax row reductions are in-lane
@@ -18,6 +20,7 @@
 // transpose loads).  Pbar never leaves registers.
 #include "ldc_device.hpp"
 #include "ldc_internal.h"
+#include "ldc_pipeline.hpp"
 
 namespace ldc {
 
@@ -26,8 +29,8 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   constexpr int BQ = 16 * NW;
   constexpr int R = BQ + kHalo;
   constexpr int NT = NW * kWave;
-  constexpr int S = lds_stride<T, D>();
-  __shared__ __attribute__((aligned(16))) T s_x[R * S];
+  __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
+  __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
   __shared__ int s_doc[R];
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
@@ -43,7 +46,20 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   const int brow = 16 * w;       // LDS row of this wave's band start (token qw - 112)
   const int t = q0 + 16 * w + n; // this lane's query
   const bool tval = t < a.T;
+  const int tc = tval ? t : a.T - 1;  // a valid row for unconditional loads
   const int H = a.H;
+  const int Hp = (H + 1) & ~1;
+
+  auto issue = [&](int phase, int h, bool on, auto bc) {
+    T* buf = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    issue_tile<T, D, R, NW>(buf, phase == 0 ? k : v, span0, a.T, H, h, on);
+  };
+  auto issue_next = [&](int phase, int j, auto bc) {
+    const NextStage ns = next_stage(phase, j, H, Hp, 2);
+    issue(ns.phase == 0 ? 0 : 1, ns.head >= 0 ? ns.head : 0, ns.head >= 0,
+          Buf<1 - decltype(bc)::value>{});
+  };
+  issue(0, 0, true, Buf<0>{});
 
   for (int r = threadIdx.x; r < R; r += NT) {
     const int s = span0 + r;
@@ -53,7 +69,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
 
   // Admission mask of this lane's 32 band entries: bit 4b+i <-> key row brow+16b+4g+i.
   uint32_t mbits = 0;
-  if (tval) {
+  {
     const int dt = s_doc[brow + kHalo + n];
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
@@ -61,7 +77,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = brow + 16 * b + 4 * g + i;
         const int s = span0 + r;
-        const bool ok = s >= 0 && s <= t && t - s < a.window && s_doc[r] == dt;
+        const bool ok = tval & (s >= 0) & (s <= t) & (t - s < a.window) & (s_doc[r] == dt);
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
@@ -74,20 +90,24 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
 
-  // ---- pass 1: per-head scores, softmax, composition into Pbar^T ----
-  for (int h = 0; h < H; ++h) {
-    __syncthreads();
-    stage_rows<T, D, R, NT>(s_x, k, span0, a.T, H, h);
+  // ---- phase 0 (K_h staged): scores, softmax, composition into Pbar^T ----
+  for_stage_pairs(Hp, [&](int j, auto bc) {
+    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    wait_dma();
+    const bool real = j < H;
+    const int hh = real ? j : 0;
     RowFrag<T, D> qf;
-    load_row_frag<T, D>(qf, q + ((size_t)t * H + h) * D, g, tval);
-    const float ch = tval ? a.c[(size_t)t * H + h] : 0.f;
-    __syncthreads();
+    load_row_frag<T, D>(qf, q + ((size_t)tc * H + hh) * D, g);
+    const float ch = a.c[(size_t)tc * H + hh];  // rows t >= T are fully masked (coef 0)
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next(0, j, bc);
+    if (!real) return;
 
     f32x4 sc[kKeyBlocks];
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       sc[b] = zero4();
-      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], s_x + (brow + 16 * b + n) * S, qf, g);
+      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], cur, brow + 16 * b + n, qf, g);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -113,21 +133,25 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[b][i] += coef * sc[b][i];
-  }
+  });
 
   BandOperand<T> pop;
   pop.set(pb);
 
-  // ---- pass 2: O^T_h = V_h^T Pbar^T, scaled by G ----
-  for (int h = 0; h < H; ++h) {
-    __syncthreads();
-    stage_rows<T, D, R, NT>(s_x, v, span0, a.T, H, h);
-    const float gh = tval ? a.g[(size_t)t * H + h] : 0.f;
-    __syncthreads();
+  // ---- phase 1 (V_h staged): O^T_h = V_h^T Pbar^T, scaled by G ----
+  for_stage_pairs(Hp, [&](int j, auto bc) {
+    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    wait_dma();
+    const bool real = j < H;
+    const float gh = a.g[(size_t)tc * H + (real ? j : 0)];
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next(1, j, bc);
+    if (!real) return;
     f32x4 acc[D / 16];
-    mma_tcontract<T, D>(acc, s_x, brow, pop, live, g, n);
-    if (tval) store_row_f32<T, D>(o + ((size_t)t * H + h) * D, acc, gh, g);
-  }
+    mma_tcontract<T, D>(acc, cur, brow, pop, live, g, n);
+    if (tval) store_row_f32<T, D>(o + ((size_t)t * H + j) * D, acc, gh, g);
+  });
+  wait_dma();  // no DMA may land in LDS after the workgroup ends
 }
 
 template <typename T, int D, int NW>
@@ -143,7 +167,7 @@ hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, hipStream_t st) {
     if (d == 128) return launch_fwd<bf16_t, 128, 8>(a, st);
     if (d == 64) return launch_fwd<bf16_t, 64, 8>(a, st);
   } else {
-    if (d == 128) return launch_fwd<float, 128, 4>(a, st);
+    if (d == 128) return launch_fwd<float, 128, 2>(a, st);
     if (d == 64) return launch_fwd<float, 64, 4>(a, st);
     if (d == 16) return launch_fwd<float, 16, 4>(a, st);
   }

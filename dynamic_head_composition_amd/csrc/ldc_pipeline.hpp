@@ -1,0 +1,47 @@
+// Double-buffered stage pipeline shared by the Lightweight DC kernels.
+//
+// A kernel walks "stages": one head of one staged tensor each, grouped in
+// phases (e.g. all heads' K, then all heads' V).  Stage j of a phase computes
+// from LDS buffer j%2 while the DMA of the next stage fills the other buffer.
+// Buffer roles must be compile-time constants: with a runtime-selected buffer
+// the compiler can no longer tell that the reads of one buffer do not alias
+// the DMA into the other and serialises them.  Phases therefore run over an
+// even number of stages (a trailing empty stage when H is odd), two stages
+// per loop iteration, and each stage body receives its buffer index as a type.
+#pragma once
+
+#include <type_traits>
+
+namespace ldc {
+
+template <int B>
+using Buf = std::integral_constant<int, B>;
+
+// Loop j over [0, Hp) two stages at a time (Hp even); body(j, Buf<j%2>).
+template <typename F>
+__device__ __forceinline__ void for_stage_pairs(int Hp, F&& body) {
+  for (int j = 0; j < Hp; j += 2) {
+    body(j, Buf<0>{});
+    body(j + 1, Buf<1>{});
+  }
+}
+
+// The stage that follows stage j of phase `phase` in padded order, as
+// (phase, head); head < 0 when nothing must be loaded now: the end of the
+// pipeline, or an empty padding stage (the stage after it is then issued by
+// the empty stage, whose buffer is the other one).  Callers still issue a
+// zero-byte DMA in that case, so every stage has the same memory-op sequence.
+struct NextStage {
+  int phase, head;
+};
+__device__ __forceinline__ NextStage next_stage(int phase, int j, int H, int Hp, int nphases) {
+  int np = phase, nj = j + 1;
+  if (nj == Hp) {
+    np = phase + 1;
+    nj = 0;
+  }
+  if (np >= nphases || nj >= H) return {np, -1};
+  return {np, nj};
+}
+
+}  // namespace ldc
