@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, help="truncate the stream (quick runs only)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB once (a plain copy kernel of "
+                         "known traffic, to calibrate HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -162,6 +165,13 @@ def main():
         if evs:
             evs[3].record()
 
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -179,7 +189,6 @@ def main():
     kernel_ms = {kname: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                  for j, kname in enumerate(KERNELS)}
     pairs = valid_pairs(w.doc, w.window)
-    flops = {"ldc_fwd": 4.0 * H * d * pairs, "ldc_bwd_q": None, "ldc_bwd_kv": None}
     total_flops = 14.0 * H * d * pairs
     bpt = algorithmic_bytes_per_token(H, d, elem)
     per_kernel = {}
