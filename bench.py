@@ -33,7 +33,7 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 MFMA_F32_PEAK_TFLOPS = 157.3
 METRIC = "LDC attention fwd+bwd tokens/s on 1 MI355X (GPT-2-small shape); % MFMA peak"
 KERNELS = ("ldc_fwd", "ldc_bwd_q", "ldc_bwd_kv")
-SOURCES = ("ldc_device.hpp", "ldc_fwd.hip", "ldc_bwd.hip", "ldc_internal.h")
+SOURCES = ("ldc_device.hpp", "ldc_pipeline.hpp", "ldc_fwd.hip", "ldc_bwd.hip", "ldc_internal.h")
 
 
 def log(*a):

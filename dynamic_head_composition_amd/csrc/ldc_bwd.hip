@@ -56,6 +56,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   const int tc = tval ? t : a.T - 1;
   const int H = a.H;
   const int Hp = (H + 1) & ~1;
+  const LaneOffsets<T, D> lo(g, n);
 
   // phases: 0 = K (P_h, Pbar), 1 = V (dPbar, dG), 2 = K (dC, dS, dQ)
   auto issue = [&](int phase, int h, bool on, auto bc) {
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       sc[b] = zero4();
-      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], cur, brow + 16 * b + n, qf, g);
+      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], cur, brow + 16 * b, lo, qf);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -132,21 +133,48 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   f32x4 pb[kKeyBlocks];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
+  // Per-head register operands are loaded one stage ahead (slot j%2 holds head j).
+  RowFrag<T, D> fb[2];
+  float sb[2];
+  auto preload = [&](const T* src, const float* scal) {
+    load_row_frag<T, D>(fb[0], src + (size_t)tc * H * D, g);
+    sb[0] = scal[(size_t)tc * H];
+  };
+  auto prefetch = [&](int j, auto bc, const T* src, const float* scal) {
+    constexpr int B = decltype(bc)::value;
+    const int hn = j + 1 < H ? j + 1 : 0;
+    load_row_frag<T, D>(fb[1 - B], src + ((size_t)tc * H + hn) * D, g);
+    sb[1 - B] = scal[(size_t)tc * H + hn];
+  };
+
+  // Small per-row results (statistics, dG, dC) and the dQ row are stored at
+  // the start of the next stage, after its barrier: the stage wait (vmcnt 0)
+  // then never waits for fresh stores.
+  float stat_mx = 0.f, stat_inv = 0.f;
+  int stat_h = -1;
+  auto flush_stats = [&]() {
+    if (stat_h >= 0 && tval && g == 0) a.stats[(size_t)t * H + stat_h] = float2{stat_mx, stat_inv};
+    stat_h = -1;
+  };
+  preload(q, a.c);
   for_stage_pairs(Hp, [&](int j, auto bc) {
-    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    constexpr int B = decltype(bc)::value;
+    const T* cur = B == 0 ? s_x0 : s_x1;
     wait_dma();
     const bool real = j < H;
-    const int hh = real ? j : 0;
-    RowFrag<T, D> qf;
-    load_row_frag<T, D>(qf, q + ((size_t)tc * H + hh) * D, g);
-    const float ch = a.c[(size_t)tc * H + hh];
+    prefetch(j, bc, q, a.c);
+    flush_stats();
     __builtin_amdgcn_sched_barrier(0);
     issue_next(0, j, bc);
     if (!real) return;
+    const RowFrag<T, D>& qf = fb[B];
+    const float ch = sb[B];
     f32x4 sc[kKeyBlocks];
     float mx, inv;
     softmax_head(sc, cur, qf, mx, inv);
-    if (tval && g == 0) a.stats[(size_t)t * H + j] = float2{mx, inv};
+    stat_mx = mx;
+    stat_inv = inv;
+    stat_h = j;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
@@ -157,22 +185,31 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   f32x4 dpb[kKeyBlocks];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) dpb[b] = zero4();
+  flush_stats();
+  float dg_val = 0.f;
+  int dg_h = -1;
+  auto flush_dg = [&]() {
+    if (dg_h >= 0 && tval && g == 0) a.dg[(size_t)t * H + dg_h] = dg_val;
+    dg_h = -1;
+  };
+  preload(dO, a.g);
   for_stage_pairs(Hp, [&](int j, auto bc) {
-    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    constexpr int B = decltype(bc)::value;
+    const T* cur = B == 0 ? s_x0 : s_x1;
     wait_dma();
     const bool real = j < H;
-    const int hh = real ? j : 0;
-    RowFrag<T, D> df;
-    load_row_frag<T, D>(df, dO + ((size_t)tc * H + hh) * D, g);
-    const float gh = a.g[(size_t)tc * H + hh];
+    prefetch(j, bc, dO, a.g);
+    flush_dg();
     __builtin_amdgcn_sched_barrier(0);
     issue_next(1, j, bc);
     if (!real) return;
+    const RowFrag<T, D>& df = fb[B];
+    const float gh = sb[B];
     float dgs = 0.f;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       if (!((live >> b) & 1u)) continue;
-      const f32x4 bt = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b + n, df, g);
+      const f32x4 bt = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, df);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // masked entries of pb are exactly 0; bt there is finite (zero-filled rows)
@@ -180,22 +217,35 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
         dpb[b][i] += gh * bt[i];
       }
     }
-    dgs = wave_sum4(dgs);
-    if (tval && g == 0) a.dg[(size_t)t * H + j] = dgs;
+    dg_val = wave_sum4(dgs);
+    dg_h = j;
   });
+  flush_dg();
 
   // ---- phase 2: recompute P_h, dC, dS, dQ ----
+  f32x4 pend[D / 16];
+  float dc_val = 0.f;
+  int pend_h = -1;
+  auto flush_dq = [&]() {
+    if (pend_h >= 0 && tval) {
+      if (g == 0) a.dc[(size_t)t * H + pend_h] = dc_val;
+      store_row_f32<T, D>(a.dq + ((size_t)t * H + pend_h) * D, pend, a.scale, g);
+    }
+    pend_h = -1;
+  };
+  preload(q, a.c);
   for_stage_pairs(Hp, [&](int j, auto bc) {
-    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    constexpr int B = decltype(bc)::value;
+    const T* cur = B == 0 ? s_x0 : s_x1;
     wait_dma();
     const bool real = j < H;
-    const int hh = real ? j : 0;
-    RowFrag<T, D> qf;
-    load_row_frag<T, D>(qf, q + ((size_t)tc * H + hh) * D, g);
-    const float ch = a.c[(size_t)tc * H + hh];
+    prefetch(j, bc, q, a.c);
+    flush_dq();
     __builtin_amdgcn_sched_barrier(0);
     issue_next(2, j, bc);
     if (!real) return;
+    const RowFrag<T, D>& qf = fb[B];
+    const float ch = sb[B];
     f32x4 sc[kKeyBlocks];
     float mx, inv;
     softmax_head(sc, cur, qf, mx, inv);
@@ -205,17 +255,17 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dcs += sc[b][i] * dpb[b][i];
     dcs = wave_sum4(dcs);
-    if (tval && g == 0) a.dc[(size_t)t * H + j] = dcs;
+    dc_val = dcs;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[b][i] = ch * sc[b][i] * (dpb[b][i] - dcs);
     BandOperand<T> dso;
     dso.set(sc);
-    f32x4 acc[D / 16];
-    mma_tcontract<T, D>(acc, cur, brow, dso, live, g, n);
-    if (tval) store_row_f32<T, D>(a.dq + ((size_t)t * H + j) * D, acc, a.scale, g);
+    mma_tcontract<T, D>(pend, cur, brow, lo, dso, live, g, n);
+    pend_h = j;
   });
+  flush_dq();
   wait_dma();
 }
 
@@ -255,6 +305,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   const int sc_ = sval ? s : a.T - 1;
   const int H = a.H;
   const int Hp = (H + 1) & ~1;
+  const LaneOffsets<T, D> lo(g, n);
 
   // phases: 0 = Q (Pbar), 1 = dO (dV, dPbar), 2 = Q (dS, dK)
   auto issue = [&](int phase, int h, bool on, auto bc) {
@@ -305,7 +356,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       p[b] = zero4();
-      if ((live >> b) & 1u) p[b] = mma_dcontract<T, D>(p[b], cur, brow + 16 * b + n, kf, g);
+      if ((live >> b) & 1u) p[b] = mma_dcontract<T, D>(p[b], cur, brow + 16 * b, lo, kf);
       const float4 mx = rows4(sc, SC_MX, b), inv = rows4(sc, SC_INV, b);
       const float mxv[4] = {mx.x, mx.y, mx.z, mx.w}, invv[4] = {inv.x, inv.y, inv.z, inv.w};
 #pragma unroll
@@ -344,6 +395,14 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   f32x4 dpb[kKeyBlocks];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) dpb[b] = zero4();
+  // A stage's output row is stored at the start of the next stage, after its
+  // barrier: the stage wait (vmcnt 0) then never waits for fresh stores.
+  f32x4 pend[D / 16];
+  int pend_h = -1;
+  auto flush = [&](float* dst, float scale) {
+    if (pend_h >= 0 && sval) store_row_f32<T, D>(dst + ((size_t)s * H + pend_h) * D, pend, scale, g);
+    pend_h = -1;
+  };
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
     const T* cur = B == 0 ? s_x0 : s_x1;
@@ -352,6 +411,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     const bool real = j < H;
     RowFrag<T, D> vf;
     load_row_frag<T, D>(vf, v + ((size_t)sc_ * H + (real ? j : 0)) * D, g);
+    flush(a.dv, 1.f);
     __builtin_amdgcn_sched_barrier(0);
     issue_next(1, j, bc);
     if (!real) return;
@@ -364,14 +424,13 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
       }
       BandOperand<T> op;
       op.set(gp);
-      f32x4 acc[D / 16];
-      mma_tcontract<T, D>(acc, cur, brow, op, live, g, n);
-      if (sval) store_row_f32<T, D>(a.dv + ((size_t)s * H + j) * D, acc, 1.f, g);
+      mma_tcontract<T, D>(pend, cur, brow, lo, op, live, g, n);
+      pend_h = j;
     }
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       if (!((live >> b) & 1u)) continue;
-      const f32x4 bt = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b + n, vf, g);
+      const f32x4 bt = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, vf);
       const float4 g4 = rows4(sc, SC_G, b);
       const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
@@ -380,6 +439,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   });
 
   // ---- phase 2 (Q_h staged): P_h, dS_h, dK_h = scale dS_h^T Q_h ----
+  bool first2 = true;
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
     const T* cur = B == 0 ? s_x0 : s_x1;
@@ -388,6 +448,8 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     const bool real = j < H;
     RowFrag<T, D> kf;
     load_row_frag<T, D>(kf, k + ((size_t)sc_ * H + (real ? j : 0)) * D, g);
+    flush(first2 ? a.dv : a.dk, first2 ? 1.f : a.scale);
+    first2 = false;
     __builtin_amdgcn_sched_barrier(0);
     issue_next(2, j, bc);
     if (!real) return;
@@ -402,10 +464,10 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     }
     BandOperand<T> dso;
     dso.set(p);
-    f32x4 acc[D / 16];
-    mma_tcontract<T, D>(acc, cur, brow, dso, live, g, n);
-    if (sval) store_row_f32<T, D>(a.dk + ((size_t)s * H + j) * D, acc, a.scale, g);
+    mma_tcontract<T, D>(pend, cur, brow, lo, dso, live, g, n);
+    pend_h = j;
   });
+  flush(a.dk, a.scale);
   wait_dma();
 }
 

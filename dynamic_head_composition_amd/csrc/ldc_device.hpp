@@ -102,17 +102,29 @@ __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_max4(float x) {
-  // reduce over the four 16-lane groups (lanes n, n+16, n+32, n+48)
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Reductions over the four 16-lane groups (lanes n, n+16, n+32, n+48) with
+// the gfx950 lane-swap instructions (VALU only, no LDS round trip):
+// permlane16_swap(x, x) returns {x of this lane or of lane^16} in some order,
+// permlane32_swap(x, x) likewise for lane^32, so op(r[0], r[1]) combines the
+// pair without a lane-dependent select.
+__device__ __forceinline__ float swap16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_sum4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+__device__ __forceinline__ float swap32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float swap16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_max4(float x) { return swap32_max(swap16_max(x)); }
+__device__ __forceinline__ float wave_sum4(float x) { return swap32_sum(swap16_sum(x)); }
 
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float b0, float b1,
                                         float b2, float b3) {
@@ -223,27 +235,54 @@ __device__ __forceinline__ void load_row_frag(RowFrag<T, D>& f, const T* __restr
   }
 }
 
-// acc += A x B for a contraction over the head dimension, where the A operand
-// row (m = this lane's n) is tile row `r` and B is the fragment f.
+// Per-lane byte offsets of the LDS reads, relative to a tile row that is a
+// multiple of 16 (every swizzle depends on row & 15 only).  With these, each
+// read is tile + uniform row offset + one of a few lane offsets + an
+// immediate, which keeps the address registers to a handful.
 template <typename T, int D>
-__device__ __forceinline__ f32x4 mma_dcontract(f32x4 acc, const T* tile, int r,
-                                               const RowFrag<T, D>& f, int g) {
+struct LaneOffsets {
   using TL = Tile<T, D>;
-  const char* base = reinterpret_cast<const char*>(tile);
+  static constexpr int ND = Elem<T>::bf16 ? D / 32 : D / 16;  // score-operand reads per row
+  static constexpr int NT = Elem<T>::bf16 ? D / 32 : 1;       // transpose-read column groups
+  int dk[ND];  // score operand: row n of the block, chunk of k-step kk
+  int tr[NT];  // value operand (bf16): row 4g + n/4, chunk 4p + n%4
+  __device__ __forceinline__ LaneOffsets(int g, int n) {
+    if constexpr (Elem<T>::bf16) {
+#pragma unroll
+      for (int kk = 0; kk < ND; ++kk) dk[kk] = n * TL::row_bytes + TL::pos(n, 4 * kk + g) * 16;
+      const int rr = n >> 2, bq = n & 3, row = 4 * g + rr;
+#pragma unroll
+      for (int p = 0; p < NT; ++p) tr[p] = row * TL::row_bytes + TL::pos(row, 4 * p + bq) * 16;
+    } else {
+#pragma unroll
+      for (int c = 0; c < ND; ++c) dk[c] = n * TL::row_bytes + TL::pos(n, g * (D / 16) + c) * 16;
+      tr[0] = 0;
+    }
+  }
+};
+
+// acc += A x B for a contraction over the head dimension, where the A operand
+// row (m = this lane's n) is tile row row16 + n (row16 a multiple of 16) and
+// B is the fragment f.
+template <typename T, int D>
+__device__ __forceinline__ f32x4 mma_dcontract(f32x4 acc, const T* tile, int row16,
+                                               const LaneOffsets<T, D>& lo, const RowFrag<T, D>& f) {
+  using TL = Tile<T, D>;
+  const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
   if constexpr (Elem<T>::bf16) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      uint4 u = *reinterpret_cast<const uint4*>(base + TL::off(r, 32 * kk + 8 * g));
+      uint4 u = *reinterpret_cast<const uint4*>(base + lo.dk[kk]);
       acc = mma(__builtin_bit_cast(bf16x8, u), f.v[kk], acc);
     }
   } else {
 #pragma unroll
-    for (int kk = 0; kk < D / 4; kk += 4) {
-      float4 u = *reinterpret_cast<const float4*>(base + TL::off(r, g * (D / 4) + kk));
-      acc = mma(u.x, f.v[kk], acc);
-      acc = mma(u.y, f.v[kk + 1], acc);
-      acc = mma(u.z, f.v[kk + 2], acc);
-      acc = mma(u.w, f.v[kk + 3], acc);
+    for (int c = 0; c < D / 16; ++c) {
+      float4 u = *reinterpret_cast<const float4*>(base + lo.dk[c]);
+      acc = mma(u.x, f.v[4 * c], acc);
+      acc = mma(u.y, f.v[4 * c + 1], acc);
+      acc = mma(u.z, f.v[4 * c + 2], acc);
+      acc = mma(u.w, f.v[4 * c + 3], acc);
     }
   }
   return acc;
@@ -288,29 +327,28 @@ struct BandOperand<float> {
 //   fp32: acc[db][i]   <-> d = 16db + 4g + i
 // `live` bit b set when token block b holds any admitted pair for this wave.
 template <typename T, int D>
-__device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* tile, int base_row,
-                                              const BandOperand<T>& P, uint32_t live, int g,
-                                              int n) {
+__device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* tile, int row16,
+                                              const LaneOffsets<T, D>& lo, const BandOperand<T>& P,
+                                              uint32_t live, int g, int n) {
   using TL = Tile<T, D>;
-  const char* base = reinterpret_cast<const char*>(tile);
+  const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
 #pragma unroll
   for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
   if constexpr (Elem<T>::bf16) {
     typedef __attribute__((address_space(3))) bf16x4 lds_v4;
-    const int rr = n >> 2, bq = n & 3;
 #pragma unroll
     for (int ks = 0; ks < kKeyBlocks / 2; ++ks) {
       if (!((live >> (2 * ks)) & 3u)) continue;
-      const int row1 = base_row + 32 * ks + 4 * g + rr;  // row1 + 16 has the same swizzle
 #pragma unroll
       for (int p = 0; p < D / 32; ++p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const char* a1 = base + TL::off(row1, 32 * p + 8 * bq + 4 * e);
+          // rows 32ks + 4g + n/4 and 16 further down: same swizzle, immediate offsets
+          const char* a1 = base + lo.tr[p] + 32 * ks * TL::row_bytes + 8 * e;
           const char* a2 = a1 + 16 * TL::row_bytes;
-          bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
-          bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a2));
-          bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
+          bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a2));
+          bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
           acc[2 * p + e] = mma(a, P.hi[ks], acc[2 * p + e]);
           acc[2 * p + e] = mma(a, P.lo[ks], acc[2 * p + e]);
         }
@@ -322,7 +360,7 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
       if (!((live >> b) & 1u)) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = base_row + 16 * b + 4 * g + i;
+        const int r = 16 * b + 4 * g + i;  // relative to row16
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) {
           const float x = *reinterpret_cast<const float*>(base + TL::off(r, 16 * db + n));

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   const int tc = tval ? t : a.T - 1;  // a valid row for unconditional loads
   const int H = a.H;
   const int Hp = (H + 1) & ~1;
+  const LaneOffsets<T, D> lo(g, n);
 
   auto issue = [&](int phase, int h, bool on, auto bc) {
     T* buf = decltype(bc)::value == 0 ? s_x0 : s_x1;
@@ -90,24 +91,33 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
 
+  // Per-head register operands are loaded one stage ahead (slot j%2 holds
+  // head j), so their latency overlaps the previous stage's compute.
+  RowFrag<T, D> qfb[2];
+  float chb[2];  // rows t >= T are fully masked (coef 0), their loads use row T-1
+  load_row_frag<T, D>(qfb[0], q + (size_t)tc * H * D, g);
+  chb[0] = a.c[(size_t)tc * H];
+
   // ---- phase 0 (K_h staged): scores, softmax, composition into Pbar^T ----
   for_stage_pairs(Hp, [&](int j, auto bc) {
-    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    constexpr int B = decltype(bc)::value;
+    const T* cur = B == 0 ? s_x0 : s_x1;
     wait_dma();
     const bool real = j < H;
-    const int hh = real ? j : 0;
-    RowFrag<T, D> qf;
-    load_row_frag<T, D>(qf, q + ((size_t)tc * H + hh) * D, g);
-    const float ch = a.c[(size_t)tc * H + hh];  // rows t >= T are fully masked (coef 0)
+    const int hn = j + 1 < H ? j + 1 : 0;
+    load_row_frag<T, D>(qfb[1 - B], q + ((size_t)tc * H + hn) * D, g);
+    chb[1 - B] = a.c[(size_t)tc * H + hn];
     __builtin_amdgcn_sched_barrier(0);
     issue_next(0, j, bc);
     if (!real) return;
+    const RowFrag<T, D>& qf = qfb[B];
+    const float ch = chb[B];
 
     f32x4 sc[kKeyBlocks];
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       sc[b] = zero4();
-      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], cur, brow + 16 * b + n, qf, g);
+      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], cur, brow + 16 * b, lo, qf);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -139,18 +149,33 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   pop.set(pb);
 
   // ---- phase 1 (V_h staged): O^T_h = V_h^T Pbar^T, scaled by G ----
+  // A stage's output row is stored at the start of the next stage, after its
+  // barrier: the stage wait (vmcnt 0) then never waits for fresh stores.
+  float ghb[2];
+  ghb[0] = a.g[(size_t)tc * H];
+  f32x4 pend[D / 16];
+  int pend_h = -1;
+  auto flush = [&]() {
+    if (pend_h >= 0 && tval) store_row_f32<T, D>(o + ((size_t)t * H + pend_h) * D, pend, 1.f, g);
+    pend_h = -1;
+  };
   for_stage_pairs(Hp, [&](int j, auto bc) {
-    const T* cur = decltype(bc)::value == 0 ? s_x0 : s_x1;
+    constexpr int B = decltype(bc)::value;
+    const T* cur = B == 0 ? s_x0 : s_x1;
     wait_dma();
     const bool real = j < H;
-    const float gh = a.g[(size_t)tc * H + (real ? j : 0)];
+    ghb[1 - B] = a.g[(size_t)tc * H + (j + 1 < H ? j + 1 : 0)];
+    flush();
     __builtin_amdgcn_sched_barrier(0);
     issue_next(1, j, bc);
     if (!real) return;
-    f32x4 acc[D / 16];
-    mma_tcontract<T, D>(acc, cur, brow, pop, live, g, n);
-    if (tval) store_row_f32<T, D>(o + ((size_t)t * H + j) * D, acc, gh, g);
+    const float gh = ghb[B];
+    mma_tcontract<T, D>(pend, cur, brow, lo, pop, live, g, n);
+#pragma unroll
+    for (int r = 0; r < D / 16; ++r) pend[r] *= gh;
+    pend_h = j;
   });
+  flush();
   wait_dma();  // no DMA may land in LDS after the workgroup ends
 }
 
