@@ -53,16 +53,21 @@ def valid_pairs(doc: np.ndarray, window: int) -> int:
 
 def algorithmic_bytes_per_token(H: int, d: int, elem: int) -> dict:
     """Compulsory HBM bytes per token of each kernel: every input it must read
-    and every output it must write, once."""
+    and every output it must write, once.  The saved state of the forward is
+    512 B/token of shared-map band (2,048 four-byte words per 16 tokens) plus
+    8 B per (token, head) of softmax statistics; the backward workspace holds
+    the dPbar band (512 B/token)."""
     row = H * d
-    ch = 4 * H  # one float per (token, head)
+    ch = 4 * H    # one float per (token, head)
+    band = 512    # shared-map or dPbar band
+    stats = 2 * ch
     return {
-        # q, k, v in; c, g, doc in; o (fp32) out
-        "ldc_fwd": 3 * row * elem + 2 * ch + 4 + row * 4,
-        # q, k, v, dO in; c, g, doc in; dq out; dc, dg out; statistics out
-        "ldc_bwd_q": 4 * row * elem + 2 * ch + 4 + row * 4 + 2 * ch + 2 * ch,
-        # q, k, v, dO in; c, g, dc, statistics, doc in; dk, dv out
-        "ldc_bwd_kv": 4 * row * elem + 3 * ch + 2 * ch + 4 + 2 * row * 4,
+        # q, k, v, c, g, doc in; o (fp32), saved band + statistics out
+        "ldc_fwd": 3 * row * elem + 2 * ch + 4 + row * 4 + band + stats,
+        # q, k, v, dO, c, g, doc, saved band + statistics in; dq, dc, dg, dPbar band out
+        "ldc_bwd_q": 4 * row * elem + 2 * ch + 4 + band + stats + row * 4 + 2 * ch + band,
+        # q, k, dO, c, g, dc, statistics, doc, both bands in; dk, dv out
+        "ldc_bwd_kv": 3 * row * elem + 3 * ch + stats + 4 + 2 * band + 2 * row * 4,
     }
 
 
@@ -150,18 +155,19 @@ def main():
              torch.empty((T, H, d), **f32), torch.empty((T, H), **f32), torch.empty((T, H), **f32))
     code = ldc.LDC_BF16 if w.dtype == "bf16" else ldc.LDC_F32
     ws = torch.empty(max(16, ldc.workspace_bytes(code, T, H, d, w.window)), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(max(16, ldc.saved_bytes(code, T, H, d, w.window)), dtype=torch.uint8, device="cuda")
     ins = (x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"])
 
     def step(evs=None):
         if evs:
             evs[0].record()
-        ldc.fwd(*ins, window=w.window, scale=w.scale, out=o)
+        ldc.fwd(*ins, window=w.window, scale=w.scale, out=o, saved=saved)
         if evs:
             evs[1].record()
-        ldc.bwd(*ins, x["do"], window=w.window, scale=w.scale, out=grads, workspace=ws, part="q")
+        ldc.bwd(*ins, saved, x["do"], window=w.window, scale=w.scale, out=grads, workspace=ws, part="q")
         if evs:
             evs[2].record()
-        ldc.bwd(*ins, x["do"], window=w.window, scale=w.scale, out=grads, workspace=ws, part="kv")
+        ldc.bwd(*ins, saved, x["do"], window=w.window, scale=w.scale, out=grads, workspace=ws, part="kv")
         if evs:
             evs[3].record()
 

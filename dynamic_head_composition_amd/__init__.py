@@ -5,9 +5,10 @@ only marshals arguments: shapes, dtypes and device pointers of torch tensors,
 and the current HIP stream.  Every step of the layer runs in the HIP kernels;
 there is no fallback — if the library is missing the calls raise.
 
-    o = fwd(q, k, v, c, g, doc_ids)                 # [T,H,d]
-    dq, dk, dv, dc, dg = bwd(q, k, v, c, g, doc_ids, do)
-    o = ldc_attention(q, k, v, c, g, doc_ids)       # autograd-aware
+    o = fwd(q, k, v, c, g, doc_ids)                        # [T,H,d] float32
+    o, saved = fwd(q, k, v, c, g, doc_ids, save=True)      # + state for bwd
+    dq, dk, dv, dc, dg = bwd(q, k, v, c, g, doc_ids, saved, do)
+    o = ldc_attention(q, k, v, c, g, doc_ids)              # autograd-aware
 
 The layer is the one the AITNT page "一个国产AI小透明，连续两次刷新NanoGPT
 Speedrun世界纪录" describes in section "第二刀-砍层内" (Lightweight DC
@@ -22,7 +23,7 @@ import os
 from typing import Optional
 
 __all__ = ["fwd", "bwd", "ldc_attention", "LDCFunction", "LDCError", "load_library",
-           "workspace_bytes", "status_str", "version", "LIB_PATH",
+           "workspace_bytes", "saved_bytes", "status_str", "version", "LIB_PATH",
            "LDC_BF16", "LDC_F32"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,13 +50,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         raise RuntimeError(f"{p} is missing: build it with `python -m dynamic_head_composition_amd.build`")
     lib = ctypes.CDLL(p)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-    lib.ldc_fwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 8
+    lib.ldc_fwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 7 + [vp, sz, vp]
     lib.ldc_fwd.restype = i32
     for nm in ("ldc_bwd", "ldc_bwd_q", "ldc_bwd_kv"):
-        getattr(lib, nm).argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 12 + [vp, sz, vp]
+        getattr(lib, nm).argtypes = ([i32, i64, i32, i32, i32, f32] + [vp] * 6 + [vp, sz]
+                                     + [vp] * 6 + [vp, sz, vp])
         getattr(lib, nm).restype = i32
-    lib.ldc_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
-    lib.ldc_bwd_workspace_bytes.restype = sz
+    for nm in ("ldc_bwd_workspace_bytes", "ldc_saved_bytes"):
+        getattr(lib, nm).argtypes = [i32, i64, i32, i32, i32]
+        getattr(lib, nm).restype = sz
     lib.ldc_status_str.argtypes = [i32]
     lib.ldc_status_str.restype = ctypes.c_char_p
     lib.ldc_version.argtypes = []
@@ -74,6 +77,10 @@ def version() -> int:
 
 def workspace_bytes(dtype: int, T: int, H: int, d: int, window: int = DEFAULT_WINDOW) -> int:
     return int(load_library().ldc_bwd_workspace_bytes(dtype, T, H, d, window))
+
+
+def saved_bytes(dtype: int, T: int, H: int, d: int, window: int = DEFAULT_WINDOW) -> int:
+    return int(load_library().ldc_saved_bytes(dtype, T, H, d, window))
 
 
 # ---------------------------------------------------------------------------
@@ -124,10 +131,15 @@ def _stream(q, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _buf(t):
+    return (0, 0) if t is None else (t.data_ptr(), t.numel() * t.element_size())
+
+
 def fwd(q, k, v, c, g, doc_ids, window: int = DEFAULT_WINDOW, scale: Optional[float] = None,
-        out=None, stream=None):
-    """O[t,h,:] of the layer, float32 [T,H,d].  Enqueued on `stream`
-    (default: torch's current stream), not synchronised."""
+        out=None, save: bool = False, saved=None, stream=None):
+    """O[t,h,:] of the layer, float32 [T,H,d].  With save=True (or a `saved`
+    buffer) also the state ldc_bwd needs, returned as (O, saved).  Enqueued on
+    `stream` (default: torch's current stream), not synchronised."""
     torch = _torch()
     lib = load_library()
     T, H, d = _check(q, k, v, c, g, doc_ids)
@@ -136,18 +148,23 @@ def fwd(q, k, v, c, g, doc_ids, window: int = DEFAULT_WINDOW, scale: Optional[fl
     o = torch.empty(q.shape, dtype=torch.float32, device=q.device) if out is None else out
     if o.shape != q.shape or o.dtype != torch.float32 or not o.is_contiguous():
         raise ValueError("out must be a contiguous float32 tensor shaped like q")
+    if save and saved is None:
+        saved = torch.empty(max(16, saved_bytes(_dtype_code(q), T, H, d, window)), dtype=torch.uint8,
+                            device=q.device)
+    sp, sn = _buf(saved)
     st = lib.ldc_fwd(_dtype_code(q), T, H, d, window, float(scale),
                      q.data_ptr(), k.data_ptr(), v.data_ptr(), c.data_ptr(), g.data_ptr(),
-                     doc_ids.data_ptr(), o.data_ptr(), _stream(q, stream))
+                     doc_ids.data_ptr(), o.data_ptr(), sp, sn, _stream(q, stream))
     if st != 0:
         raise LDCError(st, "ldc_fwd")
-    return o
+    return (o, saved) if saved is not None else o
 
 
-def bwd(q, k, v, c, g, doc_ids, do, window: int = DEFAULT_WINDOW, scale: Optional[float] = None,
-        out=None, workspace=None, stream=None, part: str = "all"):
-    """(dQ, dK, dV, dC, dG), all float32.  part="q" or "kv" runs one of the
-    two backward kernels only (ldc_bwd_q / ldc_bwd_kv); "all" runs both."""
+def bwd(q, k, v, c, g, doc_ids, saved, do, window: int = DEFAULT_WINDOW,
+        scale: Optional[float] = None, out=None, workspace=None, stream=None, part: str = "all"):
+    """(dQ, dK, dV, dC, dG), all float32, given `saved` from fwd(..., save=True)
+    on the same inputs.  part="q" or "kv" runs one of the two backward kernels
+    only (ldc_bwd_q / ldc_bwd_kv); "all" runs both."""
     torch = _torch()
     lib = load_library()
     T, H, d = _check(q, k, v, c, g, doc_ids, do)
@@ -161,13 +178,14 @@ def bwd(q, k, v, c, g, doc_ids, do, window: int = DEFAULT_WINDOW, scale: Optiona
     need = workspace_bytes(_dtype_code(q), T, H, d, window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    sp, sn = _buf(saved)
+    wp, wn = _buf(workspace)
     entry = {"all": lib.ldc_bwd, "q": lib.ldc_bwd_q, "kv": lib.ldc_bwd_kv}[part]
     st = entry(_dtype_code(q), T, H, d, window, float(scale),
-                     q.data_ptr(), k.data_ptr(), v.data_ptr(), c.data_ptr(), g.data_ptr(),
-                     doc_ids.data_ptr(), do.data_ptr(),
-                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dc.data_ptr(), dg.data_ptr(),
-                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                     _stream(q, stream))
+               q.data_ptr(), k.data_ptr(), v.data_ptr(), c.data_ptr(), g.data_ptr(),
+               doc_ids.data_ptr(), sp, sn, do.data_ptr(),
+               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dc.data_ptr(), dg.data_ptr(),
+               wp, wn, _stream(q, stream))
     if st != 0:
         raise LDCError(st, {"all": "ldc_bwd", "q": "ldc_bwd_q", "kv": "ldc_bwd_kv"}[part])
     return dq, dk, dv, dc, dg
@@ -182,14 +200,16 @@ def _make_function():
 
         @staticmethod
         def forward(ctx, q, k, v, c, g, doc_ids, window=DEFAULT_WINDOW, scale=None):
-            ctx.save_for_backward(q, k, v, c, g, doc_ids)
+            o, saved = fwd(q, k, v, c, g, doc_ids, window, scale, save=True)
+            ctx.save_for_backward(q, k, v, c, g, doc_ids, saved)
             ctx.window, ctx.scale = window, scale
-            return fwd(q, k, v, c, g, doc_ids, window, scale).to(q.dtype)
+            return o.to(q.dtype)
 
         @staticmethod
         def backward(ctx, do):
-            q, k, v, c, g, doc = ctx.saved_tensors
-            dq, dk, dv, dc, dg = bwd(q, k, v, c, g, doc, do.contiguous().to(q.dtype), ctx.window, ctx.scale)
+            q, k, v, c, g, doc, saved = ctx.saved_tensors
+            dq, dk, dv, dc, dg = bwd(q, k, v, c, g, doc, saved, do.contiguous().to(q.dtype),
+                                     ctx.window, ctx.scale)
             return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dc, dg, None, None, None
 
     return LDCFunction

@@ -49,14 +49,19 @@ const char* ldc_status_str(int status) {
   }
 }
 
+size_t ldc_saved_bytes(int dtype, int64_t T, int H, int d, int window) {
+  if (check_common(dtype, T, H, d, window) != LDC_OK) return 0;
+  return ldc::saved_band_bytes(T) + (size_t)T * (size_t)H * sizeof(float2);
+}
+
 size_t ldc_bwd_workspace_bytes(int dtype, int64_t T, int H, int d, int window) {
   if (check_common(dtype, T, H, d, window) != LDC_OK) return 0;
-  return (size_t)T * (size_t)H * sizeof(float2);
+  return ldc::saved_band_bytes(T);
 }
 
 int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale, const void* q,
             const void* k, const void* v, const float* c, const float* g, const int32_t* doc_ids,
-            float* o, void* stream) {
+            float* o, void* saved, size_t saved_bytes, void* stream) {
   int st = check_common(dtype, T, H, d, window);
   if (st != LDC_OK) return st;
   if (T == 0) return LDC_OK;
@@ -65,15 +70,23 @@ int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale, const v
     if (!p) return LDC_ERR_NULL;
   for (const void* p : ptrs)
     if (!aligned16(p)) return LDC_ERR_ALIGN;
-  ldc::FwdArgs a{(int)T, H, window, scale, q, k, v, c, g, doc_ids, o};
+  if (saved) {
+    if (saved_bytes < ldc_saved_bytes(dtype, T, H, d, window)) return LDC_ERR_WORKSPACE;
+    if (!aligned16(saved)) return LDC_ERR_ALIGN;
+  }
+  uint32_t* band = static_cast<uint32_t*>(saved);
+  float2* stats = saved ? reinterpret_cast<float2*>(static_cast<char*>(saved) + ldc::saved_band_bytes(T))
+                        : nullptr;
+  ldc::FwdArgs a{(int)T, H, window, scale, q, k, v, c, g, doc_ids, o, band, stats};
   hipError_t e = ldc::fwd_dispatch(dtype, d, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
 
 static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, float scale,
                      const void* q, const void* k, const void* v, const float* c, const float* g,
-                     const int32_t* doc_ids, const void* dO, float* dq, float* dk, float* dv,
-                     float* dc, float* dg, void* workspace, size_t workspace_bytes, void* stream) {
+                     const int32_t* doc_ids, const void* saved, size_t saved_bytes, const void* dO,
+                     float* dq, float* dk, float* dv, float* dc, float* dg, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   int st = check_common(dtype, T, H, d, window);
   if (st != LDC_OK) return st;
   if (T == 0) return LDC_OK;
@@ -82,23 +95,28 @@ static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, 
     if (!p) return LDC_ERR_NULL;
   for (const void* p : ptrs)
     if (!aligned16(p)) return LDC_ERR_ALIGN;
-  const size_t need = ldc_bwd_workspace_bytes(dtype, T, H, d, window);
-  if (!workspace || workspace_bytes < need) return LDC_ERR_WORKSPACE;
+  if (!saved || saved_bytes < ldc_saved_bytes(dtype, T, H, d, window)) return LDC_ERR_WORKSPACE;
+  if (!aligned16(saved)) return LDC_ERR_ALIGN;
+  if (!workspace || workspace_bytes < ldc_bwd_workspace_bytes(dtype, T, H, d, window))
+    return LDC_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LDC_ERR_ALIGN;
+  const uint32_t* band = static_cast<const uint32_t*>(saved);
+  const float2* stats =
+      reinterpret_cast<const float2*>(static_cast<const char*>(saved) + ldc::saved_band_bytes(T));
   ldc::BwdArgs a{(int)T, H, window, scale, q, k, v, dO, c, g, doc_ids,
-                 dq, dk, dv, dc, dg, static_cast<float2*>(workspace)};
+                 dq, dk, dv, dc, dg, band, stats, static_cast<float*>(workspace)};
   hipError_t e = ldc::bwd_dispatch(dtype, d, a, parts, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
 
 #define LDC_BWD_PARAMS                                                                          \
   int dtype, int64_t T, int H, int d, int window, float scale, const void *q, const void *k,    \
-      const void *v, const float *c, const float *g, const int32_t *doc_ids, const void *dO,    \
-      float *dq, float *dk, float *dv, float *dc, float *dg, void *workspace,                   \
-      size_t workspace_bytes, void *stream
+      const void *v, const float *c, const float *g, const int32_t *doc_ids, const void *saved, \
+      size_t saved_bytes, const void *dO, float *dq, float *dk, float *dv, float *dc, float *dg, \
+      void *workspace, size_t workspace_bytes, void *stream
 #define LDC_BWD_ARGS                                                                           \
-  dtype, T, H, d, window, scale, q, k, v, c, g, doc_ids, dO, dq, dk, dv, dc, dg, workspace,   \
-      workspace_bytes, stream
+  dtype, T, H, d, window, scale, q, k, v, c, g, doc_ids, saved, saved_bytes, dO, dq, dk, dv, dc, \
+      dg, workspace, workspace_bytes, stream
 
 int ldc_bwd(LDC_BWD_PARAMS) { return bwd_parts(3, LDC_BWD_ARGS); }
 int ldc_bwd_q(LDC_BWD_PARAMS) { return bwd_parts(1, LDC_BWD_ARGS); }

@@ -9,18 +9,19 @@
 //   dQ_h = scale dS_h K_h              dK_h  = scale dS_h^T Q_h
 //   dV_h = (G_h o Pbar)^T dO_h
 //
+// The forward pass saves the shared map (as a band of 16x16 blocks) and each
+// head's softmax statistics, so neither backward kernel recomputes Pbar.
 // Two deterministic kernels, no atomics and no zero-fill:
-//  * bwd_q  (query-centric, like the forward): each wave owns 16 queries and
-//    computes their dQ, dC, dG, plus each head's softmax statistics, which it
-//    hands to the second kernel through the workspace.  Phases over the
-//    heads: K_h staged (P_h, Pbar), V_h staged (dPbar, dG), K_h staged
-//    (P_h again, dC, dS, dQ).
+//  * bwd_q  (query-centric, like the forward): each wave owns 16 queries.
+//    Phases over the heads: V_h staged (B_h, dPbar, dG); then, with dPbar
+//    complete and written to the workspace band, K_h staged (P_h from the
+//    scores and the saved statistics, dC, dS, dQ).
 //  * bwd_kv (key-centric): each wave owns 16 keys and the 128 queries whose
-//    windows can hold them; it recomputes P_h from the statistics.  Phases:
-//    Q_h staged (Pbar), dO_h staged (dV_h and dPbar), Q_h staged (dS_h, dK_h).
-// Neither writes a T x window map to HBM: the per-pair quantities live in
-// registers of the wave that needs them.  Tiles stream into LDS by DMA,
-// double-buffered, as in the forward pass.
+//    windows can hold them; Pbar and dPbar come from the two bands.  Phases:
+//    dO_h staged (dV_h), then Q_h staged (P_h, dS_h, dK_h).
+// Neither writes a T x window x H map: per-head quantities live in registers
+// of the wave that needs them.  Tiles stream into LDS by DMA, double-buffered,
+// as in the forward pass.
 #include "ldc_device.hpp"
 #include "ldc_internal.h"
 #include "ldc_pipeline.hpp"
@@ -58,13 +59,13 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   const int Hp = (H + 1) & ~1;
   const LaneOffsets<T, D> lo(g, n);
 
-  // phases: 0 = K (P_h, Pbar), 1 = V (dPbar, dG), 2 = K (dC, dS, dQ)
+  // phases: 0 = V (dPbar, dG), 1 = K (dC, dS, dQ)
   auto issue = [&](int phase, int h, bool on, auto bc) {
     T* buf = decltype(bc)::value == 0 ? s_x0 : s_x1;
-    issue_tile<T, D, R, NW>(buf, phase == 1 ? v : k, span0, a.T, H, h, on);
+    issue_tile<T, D, R, NW>(buf, phase == 0 ? v : k, span0, a.T, H, h, on);
   };
   auto issue_next = [&](int phase, int j, auto bc) {
-    const NextStage ns = next_stage(phase, j, H, Hp, 3);
+    const NextStage ns = next_stage(phase, j, H, Hp, 2);
     issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<1 - decltype(bc)::value>{});
   };
   issue(0, 0, true, Buf<0>{});
@@ -92,116 +93,56 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
 
   const float sl2 = a.scale * kLog2e;
+  const int qb = (q0 >> 4) + w;         // this wave's 16-query block
+  const bool wval = q0 + 16 * w < a.T;  // the block holds at least one query
+  const size_t bandw = (size_t)(wval ? qb : 0) * kBandWords + (4 * g) * 16 + n;
 
-  // Scores of head h for this lane's query from tile `cur`, softmax-normalised in place.
-  auto softmax_head = [&](f32x4 (&sc)[kKeyBlocks], const T* cur, const RowFrag<T, D>& qf,
-                          float& mx_out, float& inv_out) {
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      sc[b] = zero4();
-      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], cur, brow + 16 * b, lo, qf);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[b][i] *= sl2;
-        if ((mbits >> (4 * b + i)) & 1u) mx = fmaxf(mx, sc[b][i]);
-      }
-    mx = wave_max4(mx);
-    float sum = 0.f;
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(sc[b][i] - mx) : 0.f;
-        sc[b][i] = e;
-        sum += e;
-      }
-    sum = wave_sum4(sum);
-    const float inv = sum > 0.f ? 1.f / sum : 0.f;
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[b][i] *= inv;
-    mx_out = mx;
-    inv_out = inv;
-  };
-
-  // ---- phase 0: P_h, Pbar, softmax statistics ----
+  // The shared map saved by the forward pass (masked entries are stored as 0).
   f32x4 pb[kKeyBlocks];
 #pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
+  for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[b][i] = band_decode<T>(a.band[bandw + b * 256 + i * 16]);
+
   // Per-head register operands are loaded one stage ahead (slot j%2 holds head j).
   RowFrag<T, D> fb[2];
   float sb[2];
-  auto preload = [&](const T* src, const float* scal) {
+  float2 stb[2];
+  auto preload = [&](const T* src, const float* scal, bool st) {
     load_row_frag<T, D>(fb[0], src + (size_t)tc * H * D, g);
     sb[0] = scal[(size_t)tc * H];
+    if (st) stb[0] = a.stats[(size_t)tc * H];
   };
-  auto prefetch = [&](int j, auto bc, const T* src, const float* scal) {
+  auto prefetch = [&](int j, auto bc, const T* src, const float* scal, bool st) {
     constexpr int B = decltype(bc)::value;
     const int hn = j + 1 < H ? j + 1 : 0;
     load_row_frag<T, D>(fb[1 - B], src + ((size_t)tc * H + hn) * D, g);
     sb[1 - B] = scal[(size_t)tc * H + hn];
+    if (st) stb[1 - B] = a.stats[(size_t)tc * H + hn];
   };
 
-  // Small per-row results (statistics, dG, dC) and the dQ row are stored at
-  // the start of the next stage, after its barrier: the stage wait (vmcnt 0)
-  // then never waits for fresh stores.
-  float stat_mx = 0.f, stat_inv = 0.f;
-  int stat_h = -1;
-  auto flush_stats = [&]() {
-    if (stat_h >= 0 && tval && g == 0) a.stats[(size_t)t * H + stat_h] = float2{stat_mx, stat_inv};
-    stat_h = -1;
-  };
-  preload(q, a.c);
-  for_stage_pairs(Hp, [&](int j, auto bc) {
-    constexpr int B = decltype(bc)::value;
-    const T* cur = B == 0 ? s_x0 : s_x1;
-    wait_dma();
-    const bool real = j < H;
-    prefetch(j, bc, q, a.c);
-    flush_stats();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_next(0, j, bc);
-    if (!real) return;
-    const RowFrag<T, D>& qf = fb[B];
-    const float ch = sb[B];
-    f32x4 sc[kKeyBlocks];
-    float mx, inv;
-    softmax_head(sc, cur, qf, mx, inv);
-    stat_mx = mx;
-    stat_inv = inv;
-    stat_h = j;
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[b][i] += ch * sc[b][i];
-  });
-
-  // ---- phase 1: B_h = dO_h V_h^T, dPbar, dG ----
+  // ---- phase 0 (V_h staged): B_h = dO_h V_h^T, dPbar, dG ----
+  // Small results and output rows are stored at the start of the next stage,
+  // after its barrier, so the stage wait (vmcnt 0) never waits for fresh stores.
   f32x4 dpb[kKeyBlocks];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) dpb[b] = zero4();
-  flush_stats();
   float dg_val = 0.f;
   int dg_h = -1;
   auto flush_dg = [&]() {
     if (dg_h >= 0 && tval && g == 0) a.dg[(size_t)t * H + dg_h] = dg_val;
     dg_h = -1;
   };
-  preload(dO, a.g);
+  preload(dO, a.g, false);
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
     const T* cur = B == 0 ? s_x0 : s_x1;
     wait_dma();
     const bool real = j < H;
-    prefetch(j, bc, dO, a.g);
+    prefetch(j, bc, dO, a.g, false);
     flush_dg();
     __builtin_amdgcn_sched_barrier(0);
-    issue_next(1, j, bc);
+    issue_next(0, j, bc);
     if (!real) return;
     const RowFrag<T, D>& df = fb[B];
     const float gh = sb[B];
@@ -221,8 +162,15 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     dg_h = j;
   });
   flush_dg();
+  if (wval) {
+    // dPbar of this wave's block, for the key-centric kernel
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.dband[bandw + b * 256 + i * 16] = dpb[b][i];
+  }
 
-  // ---- phase 2: recompute P_h, dC, dS, dQ ----
+  // ---- phase 1 (K_h staged): P_h, dC, dS, dQ ----
   f32x4 pend[D / 16];
   float dc_val = 0.f;
   int pend_h = -1;
@@ -233,35 +181,42 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     }
     pend_h = -1;
   };
-  preload(q, a.c);
+  preload(q, a.c, true);
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
     const T* cur = B == 0 ? s_x0 : s_x1;
     wait_dma();
     const bool real = j < H;
-    prefetch(j, bc, q, a.c);
+    prefetch(j, bc, q, a.c, true);
     flush_dq();
     __builtin_amdgcn_sched_barrier(0);
-    issue_next(2, j, bc);
+    issue_next(1, j, bc);
     if (!real) return;
     const RowFrag<T, D>& qf = fb[B];
     const float ch = sb[B];
-    f32x4 sc[kKeyBlocks];
-    float mx, inv;
-    softmax_head(sc, cur, qf, mx, inv);
+    const float2 st = stb[B];
+    f32x4 p[kKeyBlocks];
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      p[b] = zero4();
+      if ((live >> b) & 1u) p[b] = mma_dcontract<T, D>(p[b], cur, brow + 16 * b, lo, qf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p[b][i] = ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(p[b][i] * sl2 - st.x) * st.y : 0.f;
+    }
     float dcs = 0.f;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dcs += sc[b][i] * dpb[b][i];
+      for (int i = 0; i < 4; ++i) dcs += p[b][i] * dpb[b][i];
     dcs = wave_sum4(dcs);
     dc_val = dcs;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[b][i] = ch * sc[b][i] * (dpb[b][i] - dcs);
+      for (int i = 0; i < 4; ++i) p[b][i] = ch * p[b][i] * (dpb[b][i] - dcs);
     BandOperand<T> dso;
-    dso.set(sc);
+    dso.set(p);
     mma_tcontract<T, D>(pend, cur, brow, lo, dso, live, g, n);
     pend_h = j;
   });
@@ -290,7 +245,6 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
-  const T* __restrict__ v = static_cast<const T*>(a.v);
   const T* __restrict__ dO = static_cast<const T*>(a.dO);
   const float* __restrict__ stats = reinterpret_cast<const float*>(a.stats);
 
@@ -307,12 +261,12 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   const int Hp = (H + 1) & ~1;
   const LaneOffsets<T, D> lo(g, n);
 
-  // phases: 0 = Q (Pbar), 1 = dO (dV, dPbar), 2 = Q (dS, dK)
+  // phases: 0 = dO (dV), 1 = Q (dS, dK)
   auto issue = [&](int phase, int h, bool on, auto bc) {
     constexpr int B = decltype(bc)::value;
     T* buf = B == 0 ? s_x0 : s_x1;
     float* sc = B == 0 ? s_sc0 : s_sc1;
-    issue_tile<T, D, R, NW>(buf, phase == 1 ? dO : q, span0, a.T, H, h, on);
+    issue_tile<T, D, R, NW>(buf, phase == 0 ? dO : q, span0, a.T, H, h, on);
     issue_scalars<R, NW>(sc + SC_C * RP, a.c, 1, 0, span0, a.T, H, h, on);
     issue_scalars<R, NW>(sc + SC_G * RP, a.g, 1, 0, span0, a.T, H, h, on);
     issue_scalars<R, NW>(sc + SC_DC * RP, a.dc, 1, 0, span0, a.T, H, h, on);
@@ -320,7 +274,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     issue_scalars<R, NW>(sc + SC_INV * RP, stats, 2, 1, span0, a.T, H, h, on);
   };
   auto issue_next = [&](int phase, int j, auto bc) {
-    const NextStage ns = next_stage(phase, j, H, Hp, 3);
+    const NextStage ns = next_stage(phase, j, H, Hp, 2);
     issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<1 - decltype(bc)::value>{});
   };
   issue(0, 0, true, Buf<0>{});
@@ -347,54 +301,34 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
 
+  // Pbar and dPbar of this lane's (key, 4 queries) entries, from the bands:
+  // query block kq + b, key block 7 - b, 16 bytes per block.
+  f32x4 pb[kKeyBlocks], dpb[kKeyBlocks];
+  {
+    const int kq = (k0 >> 4) + w;
+    const int nqb = (a.T + 15) >> 4;
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      const int qbk = kq + b < nqb ? kq + b : nqb - 1;  // beyond the stream: masked below
+      const size_t wi = (size_t)qbk * kBandWords + (7 - b) * 256 + n * 16 + 4 * g;
+      const uint4 u = *reinterpret_cast<const uint4*>(a.band + wi);
+      const float4 d4 = *reinterpret_cast<const float4*>(a.dband + wi);
+      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool m = (mbits >> (4 * b + i)) & 1u;
+        pb[b][i] = m ? band_decode<T>(uu[i]) : 0.f;
+        dpb[b][i] = m ? dd[i] : 0.f;
+      }
+    }
+  }
+
   auto rows4 = [&](const float* sc, int field, int b) {
     return *reinterpret_cast<const float4*>(sc + field * RP + brow + 16 * b + 4 * g);
   };
   const float sl2 = a.scale * kLog2e;
-  // P_h of the staged head on this lane's band (rows = queries), from the statistics.
-  auto probs = [&](f32x4 (&p)[kKeyBlocks], const T* cur, const float* sc, const RowFrag<T, D>& kf) {
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      p[b] = zero4();
-      if ((live >> b) & 1u) p[b] = mma_dcontract<T, D>(p[b], cur, brow + 16 * b, lo, kf);
-      const float4 mx = rows4(sc, SC_MX, b), inv = rows4(sc, SC_INV, b);
-      const float mxv[4] = {mx.x, mx.y, mx.z, mx.w}, invv[4] = {inv.x, inv.y, inv.z, inv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        p[b][i] = ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(p[b][i] * sl2 - mxv[i]) * invv[i] : 0.f;
-    }
-  };
 
-  // ---- phase 0 (Q_h staged): Pbar on the band ----
-  f32x4 pb[kKeyBlocks];
-#pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
-  for_stage_pairs(Hp, [&](int j, auto bc) {
-    constexpr int B = decltype(bc)::value;
-    const T* cur = B == 0 ? s_x0 : s_x1;
-    const float* sc = B == 0 ? s_sc0 : s_sc1;
-    wait_dma();
-    const bool real = j < H;
-    RowFrag<T, D> kf;
-    load_row_frag<T, D>(kf, k + ((size_t)sc_ * H + (real ? j : 0)) * D, g);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_next(0, j, bc);
-    if (!real) return;
-    f32x4 p[kKeyBlocks];
-    probs(p, cur, sc, kf);
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      const float4 c4 = rows4(sc, SC_C, b);
-      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[b][i] += cv[i] * p[b][i];
-    }
-  });
-
-  // ---- phase 1 (dO_h staged): dV_h = (G_h o Pbar)^T dO_h, and dPbar ----
-  f32x4 dpb[kKeyBlocks];
-#pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) dpb[b] = zero4();
   // A stage's output row is stored at the start of the next stage, after its
   // barrier: the stage wait (vmcnt 0) then never waits for fresh stores.
   f32x4 pend[D / 16];
@@ -403,64 +337,62 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     if (pend_h >= 0 && sval) store_row_f32<T, D>(dst + ((size_t)s * H + pend_h) * D, pend, scale, g);
     pend_h = -1;
   };
+
+  // ---- phase 0 (dO_h staged): dV_h = (G_h o Pbar)^T dO_h ----
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
     const T* cur = B == 0 ? s_x0 : s_x1;
     const float* sc = B == 0 ? s_sc0 : s_sc1;
     wait_dma();
     const bool real = j < H;
-    RowFrag<T, D> vf;
-    load_row_frag<T, D>(vf, v + ((size_t)sc_ * H + (real ? j : 0)) * D, g);
     flush(a.dv, 1.f);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next(0, j, bc);
+    if (!real) return;
+    f32x4 gp[kKeyBlocks];
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      const float4 g4 = rows4(sc, SC_G, b);
+      gp[b] = f32x4{g4.x * pb[b][0], g4.y * pb[b][1], g4.z * pb[b][2], g4.w * pb[b][3]};
+    }
+    BandOperand<T> op;
+    op.set(gp);
+    mma_tcontract<T, D>(pend, cur, brow, lo, op, live, g, n);
+    pend_h = j;
+  });
+
+  // ---- phase 1 (Q_h staged): P_h, dS_h, dK_h = scale dS_h^T Q_h ----
+  RowFrag<T, D> kfb[2];
+  load_row_frag<T, D>(kfb[0], k + (size_t)sc_ * H * D, g);
+  bool first = true;
+  for_stage_pairs(Hp, [&](int j, auto bc) {
+    constexpr int B = decltype(bc)::value;
+    const T* cur = B == 0 ? s_x0 : s_x1;
+    const float* sc = B == 0 ? s_sc0 : s_sc1;
+    wait_dma();
+    const bool real = j < H;
+    load_row_frag<T, D>(kfb[1 - B], k + ((size_t)sc_ * H + (j + 1 < H ? j + 1 : 0)) * D, g);
+    flush(first ? a.dv : a.dk, first ? 1.f : a.scale);
+    first = false;
     __builtin_amdgcn_sched_barrier(0);
     issue_next(1, j, bc);
     if (!real) return;
-    {
-      f32x4 gp[kKeyBlocks];
-#pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b) {
-        const float4 g4 = rows4(sc, SC_G, b);
-        gp[b] = f32x4{g4.x * pb[b][0], g4.y * pb[b][1], g4.z * pb[b][2], g4.w * pb[b][3]};
-      }
-      BandOperand<T> op;
-      op.set(gp);
-      mma_tcontract<T, D>(pend, cur, brow, lo, op, live, g, n);
-      pend_h = j;
-    }
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      if (!((live >> b) & 1u)) continue;
-      const f32x4 bt = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, vf);
-      const float4 g4 = rows4(sc, SC_G, b);
-      const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dpb[b][i] += gv[i] * bt[i];
-    }
-  });
-
-  // ---- phase 2 (Q_h staged): P_h, dS_h, dK_h = scale dS_h^T Q_h ----
-  bool first2 = true;
-  for_stage_pairs(Hp, [&](int j, auto bc) {
-    constexpr int B = decltype(bc)::value;
-    const T* cur = B == 0 ? s_x0 : s_x1;
-    const float* sc = B == 0 ? s_sc0 : s_sc1;
-    wait_dma();
-    const bool real = j < H;
-    RowFrag<T, D> kf;
-    load_row_frag<T, D>(kf, k + ((size_t)sc_ * H + (real ? j : 0)) * D, g);
-    flush(first2 ? a.dv : a.dk, first2 ? 1.f : a.scale);
-    first2 = false;
-    __builtin_amdgcn_sched_barrier(0);
-    issue_next(2, j, bc);
-    if (!real) return;
+    const RowFrag<T, D>& kf = kfb[B];
     f32x4 p[kKeyBlocks];
-    probs(p, cur, sc, kf);
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
+      p[b] = zero4();
+      if ((live >> b) & 1u) p[b] = mma_dcontract<T, D>(p[b], cur, brow + 16 * b, lo, kf);
+      const float4 mx = rows4(sc, SC_MX, b), inv = rows4(sc, SC_INV, b);
       const float4 c4 = rows4(sc, SC_C, b), dc4 = rows4(sc, SC_DC, b);
+      const float mxv[4] = {mx.x, mx.y, mx.z, mx.w}, invv[4] = {inv.x, inv.y, inv.z, inv.w};
       const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, dcv[4] = {dc4.x, dc4.y, dc4.z, dc4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[b][i] = cv[i] * p[b][i] * (dpb[b][i] - dcv[i]);
+      for (int i = 0; i < 4; ++i) {
+        const float pp =
+            ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(p[b][i] * sl2 - mxv[i]) * invv[i] : 0.f;
+        p[b][i] = cv[i] * pp * (dpb[b][i] - dcv[i]);
+      }
     }
     BandOperand<T> dso;
     dso.set(p);

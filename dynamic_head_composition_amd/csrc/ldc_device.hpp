@@ -393,6 +393,42 @@ __device__ __forceinline__ void store_row_f32(float* __restrict__ row, const f32
   for (int r = 0; r < D / 16; ++r) store4(row + tcontract_d<T>(r, g), acc[r], s);
 }
 
+// ---------------------------------------------------------------------------
+// Saved shared-map band and dPbar band
+// ---------------------------------------------------------------------------
+// Per 16-query block qb: 8 key blocks kb, each a [key 16][query 16] array of
+// 4-byte words; key block kb of query block qb holds keys 16*qb - 112 + 16*kb
+// + (0..15).  Word of the shared map: bf16 path (hi | lo << 16) with
+// hi = bf16(x), lo = bf16(x - hi); fp32 path: the float.  The dPbar band
+// (float32) uses the same indexing.  Query-centric waves (lane = query n,
+// keys 4g+i of block b) touch word (4g+i)*16 + n; key-centric waves (lane =
+// key n, queries 4g+i of query block qb + b) read the 16 bytes at n*16 + 4g.
+constexpr int kBandWords = kKeyBlocks * 256;  // words per 16-query block
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+template <typename T>
+__device__ __forceinline__ uint32_t band_encode(float x) {
+  if constexpr (Elem<T>::bf16) {
+    const uint32_t h = bf16_bits_rne(x);
+    const uint32_t l = bf16_bits_rne(x - bf16_bits_to_float(h));
+    return h | (l << 16);
+  } else {
+    return __float_as_uint(x);
+  }
+}
+template <typename T>
+__device__ __forceinline__ float band_decode(uint32_t u) {
+  if constexpr (Elem<T>::bf16)
+    return bf16_bits_to_float(u & 0xffffu) + bf16_bits_to_float(u >> 16);
+  else
+    return __uint_as_float(u);
+}
+
 // Workgroup -> tile map that gives each XCD a contiguous run of tiles, so the
 // halo rows a tile shares with its neighbour are fetched through the same L2.
 // (Workgroups are dispatched to the 8 XCDs round-robin by block index.)

@@ -98,6 +98,16 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   load_row_frag<T, D>(qfb[0], q + (size_t)tc * H * D, g);
   chb[0] = a.c[(size_t)tc * H];
 
+  // Softmax statistics of each head go to the saved state for the backward
+  // pass; the store is deferred past the next stage's barrier.
+  float st_mx = 0.f, st_inv = 0.f;
+  int st_h = -1;
+  auto flush_stats = [&]() {
+    if (st_h >= 0 && a.band && tval && g == 0)
+      a.stats[(size_t)t * H + st_h] = float2{st_mx, st_inv};
+    st_h = -1;
+  };
+
   // ---- phase 0 (K_h staged): scores, softmax, composition into Pbar^T ----
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
@@ -112,6 +122,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     if (!real) return;
     const RowFrag<T, D>& qf = qfb[B];
     const float ch = chb[B];
+    flush_stats();
 
     f32x4 sc[kKeyBlocks];
 #pragma unroll
@@ -138,15 +149,28 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
         sum += e;
       }
     sum = wave_sum4(sum);
-    const float coef = sum > 0.f ? ch / sum : 0.f;
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    const float coef = ch * inv;
+    st_mx = mx;
+    st_inv = inv;
+    st_h = j;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[b][i] += coef * sc[b][i];
   });
 
+  flush_stats();
   BandOperand<T> pop;
   pop.set(pb);
+  if (a.band && q0 + 16 * w < a.T) {
+    // the wave's 16 x 128 shared map, for the backward pass
+    uint32_t* dst = a.band + (size_t)((q0 >> 4) + w) * kBandWords + (4 * g) * 16 + n;
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[b * 256 + i * 16] = band_encode<T>(pb[b][i]);
+  }
 
   // ---- phase 1 (V_h staged): O^T_h = V_h^T Pbar^T, scaled by G ----
   // A stage's output row is stored at the start of the next stage, after its

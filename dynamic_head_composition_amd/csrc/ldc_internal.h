@@ -6,6 +6,8 @@
 
 namespace ldc {
 
+constexpr size_t kBandWordsHost = 8 * 256;  // words per 16-query block
+
 struct FwdArgs {
   int T, H, window;
   float scale;
@@ -13,6 +15,8 @@ struct FwdArgs {
   const float *c, *g;
   const int32_t* doc;
   float* o;
+  uint32_t* band;  // saved shared-map band, or null (nothing saved)
+  float2* stats;   // saved [T,H] softmax statistics (with band)
 };
 
 struct BwdArgs {
@@ -22,8 +26,14 @@ struct BwdArgs {
   const float *c, *g;
   const int32_t* doc;
   float *dq, *dk, *dv, *dc, *dg;
-  float2* stats;  // [T,H] (scaled row max, 1/row sum) of each head's softmax
+  const uint32_t* band;  // shared-map band saved by the forward pass
+  const float2* stats;   // [T,H] (scaled row max, 1/row sum), saved by the forward pass
+  float* dband;          // workspace: dPbar band, written by bwd_q, read by bwd_kv
 };
+
+// Sizes of the saved state and of the backward workspace.
+inline size_t band_blocks(int64_t T) { return (size_t)((T + 15) / 16); }
+inline size_t saved_band_bytes(int64_t T) { return band_blocks(T) * kBandWordsHost * 4; }
 
 hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, hipStream_t st);
 // parts: bit 0 = query-side kernel, bit 1 = key-side kernel

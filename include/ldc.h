@@ -55,7 +55,7 @@ typedef enum {
   LDC_ERR_DTYPE = 3,       /* dtype is not an ldc_dtype value               */
   LDC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned              */
   LDC_ERR_UNSUPPORTED = 5, /* head dim not instantiated for this dtype      */
-  LDC_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required    */
+  LDC_ERR_WORKSPACE = 6,   /* saved state / workspace missing or too small  */
   LDC_ERR_HIP = 7          /* a HIP launch failed                           */
 } ldc_status;
 
@@ -67,15 +67,22 @@ typedef enum {
 /* Forward pass: writes O[T,H,d] in float32.
  * q, k, v: [T,H,d] in `dtype`; c, g: [T,H] float32; doc_ids: [T] int32.
  * scale: the softmax scale (1/sqrt(d) for the textbook choice).
+ * saved: NULL (inference: nothing saved) or a device buffer of at least
+ *   ldc_saved_bytes(...) bytes (16-byte aligned) that receives the state
+ *   ldc_bwd needs: the shared map Pbar over each 16-query block's 128-key
+ *   band (2,048 words per block; bf16 path: bf16 hi and lo parts) followed by
+ *   each head's softmax statistics [T,H] (row max in log2 units, 1/row sum).
  * O is float32 for both storage dtypes: a bf16 store alone would round
  * outputs of magnitude above ~5 by more than 2e-2. */
 int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale,
             const void* q, const void* k, const void* v,
             const float* c, const float* g, const int32_t* doc_ids,
-            float* o, void* stream);
+            float* o, void* saved, size_t saved_bytes, void* stream);
 
 /* Backward pass: given dO, writes every gradient of the forward above in
- * float32: dq, dk, dv [T,H,d] and dc, dg [T,H].  Same inputs as ldc_fwd.
+ * float32: dq, dk, dv [T,H,d] and dc, dg [T,H].  Same inputs as ldc_fwd, plus
+ * `saved` as written by ldc_fwd for these inputs (required; the backward
+ * does not recompute the shared map).
  * workspace: device scratch of at least ldc_bwd_workspace_bytes(...) bytes
  * (16-byte aligned), owned by the caller; its contents on entry do not matter
  * and are undefined on return.  The pass is deterministic: equal inputs give
@@ -83,29 +90,32 @@ int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale,
 int ldc_bwd(int dtype, int64_t T, int H, int d, int window, float scale,
             const void* q, const void* k, const void* v,
             const float* c, const float* g, const int32_t* doc_ids,
-            const void* dO,
+            const void* saved, size_t saved_bytes, const void* dO,
             float* dq, float* dk, float* dv, float* dc, float* dg,
             void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two kernels of ldc_bwd, callable one at a time (for per-kernel timing).
  * ldc_bwd is exactly ldc_bwd_q followed by ldc_bwd_kv with the same
  * arguments on the same stream:
- *   ldc_bwd_q  writes dq, dc, dg and the softmax statistics (workspace);
+ *   ldc_bwd_q  writes dq, dc, dg and dPbar (into the workspace);
  *   ldc_bwd_kv reads dc and the workspace and writes dk, dv.
  * Arguments, validation and errors as for ldc_bwd; pointers the kernel does
  * not touch are still validated. */
 int ldc_bwd_q(int dtype, int64_t T, int H, int d, int window, float scale,
               const void* q, const void* k, const void* v,
               const float* c, const float* g, const int32_t* doc_ids,
-              const void* dO,
+              const void* saved, size_t saved_bytes, const void* dO,
               float* dq, float* dk, float* dv, float* dc, float* dg,
               void* workspace, size_t workspace_bytes, void* stream);
 int ldc_bwd_kv(int dtype, int64_t T, int H, int d, int window, float scale,
                const void* q, const void* k, const void* v,
                const float* c, const float* g, const int32_t* doc_ids,
-               const void* dO,
+               const void* saved, size_t saved_bytes, const void* dO,
                float* dq, float* dk, float* dv, float* dc, float* dg,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the state ldc_fwd saves for ldc_bwd (0 for T == 0). */
+size_t ldc_saved_bytes(int dtype, int64_t T, int H, int d, int window);
 
 /* Bytes of workspace ldc_bwd needs for these sizes (0 for T == 0). */
 size_t ldc_bwd_workspace_bytes(int dtype, int64_t T, int H, int d, int window);

@@ -44,10 +44,11 @@ def run_gpu(ldc, w, backward=True, window=None):
     import torch
     x = w.torch_inputs("cuda", with_do=backward)
     win = w.window if window is None else window
-    o = ldc.fwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], window=win, scale=w.scale)
+    o, saved = ldc.fwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], window=win, scale=w.scale,
+                       save=True)
     res = {"o": o}
     if backward:
-        dq, dk, dv, dc, dg = ldc.bwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], x["do"],
+        dq, dk, dv, dc, dg = ldc.bwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], saved, x["do"],
                                      window=win, scale=w.scale)
         res.update(dq=dq, dk=dk, dv=dv, dc=dc, dg=dg)
     torch.cuda.synchronize()

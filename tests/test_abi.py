@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     lib = ldc.load_library()
     names = declared_functions()
     assert names == ["ldc_bwd", "ldc_bwd_kv", "ldc_bwd_q", "ldc_bwd_workspace_bytes", "ldc_fwd",
-                     "ldc_status_str", "ldc_version"]
+                     "ldc_saved_bytes", "ldc_status_str", "ldc_version"]
     for nm in names:
         assert hasattr(lib, nm)
     out = subprocess.run(["nm", "-D", "--defined-only", ldc.LIB_PATH], capture_output=True, text=True).stdout
@@ -40,25 +40,31 @@ def test_version_and_status_strings():
     assert "unknown" in ldc.status_str(99)
 
 
-def test_workspace_bytes():
-    assert ldc.workspace_bytes(ldc.LDC_BF16, 65536, 6, 128, 112) == 65536 * 6 * 8
+def test_workspace_and_saved_bytes():
+    band = 4096 * 2048 * 4  # 4,096 blocks of 16 queries x 2,048 words
+    assert ldc.workspace_bytes(ldc.LDC_BF16, 65536, 6, 128, 112) == band
+    assert ldc.saved_bytes(ldc.LDC_BF16, 65536, 6, 128, 112) == band + 65536 * 6 * 8
+    assert ldc.saved_bytes(ldc.LDC_F32, 17, 2, 16, 112) == 2 * 2048 * 4 + 17 * 2 * 8
     assert ldc.workspace_bytes(ldc.LDC_BF16, 0, 6, 128, 112) == 0
     assert ldc.workspace_bytes(ldc.LDC_BF16, 10, 6, 16, 112) == 0  # unsupported -> 0
 
 
-def fwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None):
+def fwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, saved=None, saved_bytes=0):
     lib = ldc.load_library()
     p = ptrs or [A] * 7
-    return lib.ldc_fwd(dtype, T, H, d, window, 0.1, *p, None)
+    return lib.ldc_fwd(dtype, T, H, d, window, 0.1, *p, saved, saved_bytes, None)
 
 
 def bwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, ws=A, ws_bytes=None,
-             entry="ldc_bwd"):
+             saved=A, saved_bytes=None, entry="ldc_bwd"):
     lib = ldc.load_library()
     p = ptrs or [A] * 12
     if ws_bytes is None:
         ws_bytes = ldc.workspace_bytes(dtype, T, H, d, window)
-    return getattr(lib, entry)(dtype, T, H, d, window, 0.1, *p, ws, ws_bytes, None)
+    if saved_bytes is None:
+        saved_bytes = ldc.saved_bytes(dtype, T, H, d, window)
+    return getattr(lib, entry)(dtype, T, H, d, window, 0.1, *p[:6], saved, saved_bytes, *p[6:],
+                               ws, ws_bytes, None)
 
 
 def bwd_q_call(**kw):
@@ -93,13 +99,22 @@ def test_bwd_workspace_errors(entry):
     assert bwd_call(ws=None, entry=entry) == 6
     assert bwd_call(ws_bytes=100, entry=entry) == 6
     assert bwd_call(ws=A + 4, entry=entry) == 4
+    assert bwd_call(saved=None, entry=entry) == 6
+    assert bwd_call(saved_bytes=100, entry=entry) == 6
+    assert bwd_call(saved=A + 4, entry=entry) == 4
+
+
+def test_fwd_saved_errors():
+    need = ldc.saved_bytes(ldc.LDC_BF16, 256, 6, 128, 112)
+    assert fwd_call(saved=A, saved_bytes=need - 16) == 6
+    assert fwd_call(saved=A + 4, saved_bytes=need) == 4
 
 
 def test_empty_stream_is_a_noop():
     # T == 0 returns before any HIP call, even with NULL pointers
     lib = ldc.load_library()
-    assert lib.ldc_fwd(0, 0, 6, 128, 112, 0.1, *([None] * 7), None) == 0
-    assert lib.ldc_bwd(0, 0, 6, 128, 112, 0.1, *([None] * 12), None, 0, None) == 0
+    assert lib.ldc_fwd(0, 0, 6, 128, 112, 0.1, *([None] * 7), None, 0, None) == 0
+    assert lib.ldc_bwd(0, 0, 6, 128, 112, 0.1, *([None] * 6), None, 0, *([None] * 6), None, 0, None) == 0
 
 
 def test_oracle_and_product_share_no_code():

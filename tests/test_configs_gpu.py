@@ -29,11 +29,12 @@ def workload(i):
 def run_full(ldc, w, backward):
     import torch
     x = w.torch_inputs("cuda", with_do=backward)
-    o = ldc.fwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], window=w.window, scale=w.scale)
+    o, saved = ldc.fwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], window=w.window,
+                       scale=w.scale, save=True)
     res = {"o": o}
     if backward:
         res.update(zip(("dq", "dk", "dv", "dc", "dg"),
-                       ldc.bwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], x["do"],
+                       ldc.bwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], saved, x["do"],
                                window=w.window, scale=w.scale)))
     torch.cuda.synchronize()
     for key, val in res.items():

@@ -150,9 +150,9 @@ def test_empty_stream(ldc):
     z = torch.empty((0, 6, 128), dtype=torch.bfloat16, device="cuda")
     zc = torch.empty((0, 6), dtype=torch.float32, device="cuda")
     zd = torch.empty((0,), dtype=torch.int32, device="cuda")
-    o = ldc.fwd(z, z, z, zc, zc, zd)
+    o, saved = ldc.fwd(z, z, z, zc, zc, zd, save=True)
     assert o.shape == (0, 6, 128)
-    out = ldc.bwd(z, z, z, zc, zc, zd, z)
+    out = ldc.bwd(z, z, z, zc, zc, zd, saved, z)
     assert out[0].shape == (0, 6, 128)
 
 
