@@ -18,6 +18,8 @@ bool head_dim_supported(int dtype, int d) {
   return d == 16 || d == 64 || d == 128;
 }
 
+bool scale_ok(float scale) { return scale > 0.f && scale < 3.0e38f; }  // positive and finite
+
 int check_common(int dtype, int64_t T, int H, int d, int window) {
   if (dtype != LDC_BF16 && dtype != LDC_F32) return LDC_ERR_DTYPE;
   if (T < 0 || H < 1 || window < 1 || window > 113) return LDC_ERR_SHAPE;
@@ -64,6 +66,7 @@ int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale, const v
             float* o, void* saved, size_t saved_bytes, void* stream) {
   int st = check_common(dtype, T, H, d, window);
   if (st != LDC_OK) return st;
+  if (!scale_ok(scale)) return LDC_ERR_SHAPE;
   if (T == 0) return LDC_OK;
   const void* ptrs[] = {q, k, v, c, g, doc_ids, o};
   for (const void* p : ptrs)
@@ -89,6 +92,7 @@ static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, 
                      size_t workspace_bytes, void* stream) {
   int st = check_common(dtype, T, H, d, window);
   if (st != LDC_OK) return st;
+  if (!scale_ok(scale)) return LDC_ERR_SHAPE;
   if (T == 0) return LDC_OK;
   const void* ptrs[] = {q, k, v, c, g, doc_ids, dO, dq, dk, dv, dc, dg};
   for (const void* p : ptrs)

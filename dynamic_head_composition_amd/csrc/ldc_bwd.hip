@@ -46,7 +46,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   const T* __restrict__ v = static_cast<const T*>(a.v);
   const T* __restrict__ dO = static_cast<const T*>(a.dO);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, n = lane & 15;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int q0 = tile * BQ;
@@ -88,9 +88,8 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  uint32_t live = 0;
-#pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
+  const uint32_t live = live_blocks(mbits);  // wave-uniform
+  const uint32_t full = full_blocks(mbits);
 
   const float sl2 = a.scale * kLog2e;
   const int qb = (q0 >> 4) + w;         // this wave's 16-query block
@@ -194,27 +193,29 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     if (!real) return;
     const RowFrag<T, D>& qf = fb[B];
     const float ch = sb[B];
-    const float2 st = stb[B];
+    const float2 st = stb[B];  // (row max in log2 units, 1/row sum) saved by the forward pass
+    // e = exp2(s*scale*log2e - max) = P_h / inv; masked entries 0
     f32x4 p[kKeyBlocks];
+    float dcs = 0.f;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       p[b] = zero4();
       if ((live >> b) & 1u) p[b] = mma_dcontract<T, D>(p[b], cur, brow + 16 * b, lo, qf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        p[b][i] = ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(p[b][i] * sl2 - st.x) * st.y : 0.f;
+      for (int i = 0; i < 4; ++i) p[b][i] = exp2_scaled(p[b][i], sl2, st.x);  // as in the forward pass
+      if (!((full >> b) & 1u))
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[b][i] = admitted(mbits, b, i) ? p[b][i] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dcs = fmaf(p[b][i], dpb[b][i], dcs);
     }
-    float dcs = 0.f;
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dcs += p[b][i] * dpb[b][i];
-    dcs = wave_sum4(dcs);
+    dcs = wave_sum4(dcs) * st.y;  // dC = sum_s P_h dPbar
     dc_val = dcs;
+    const float cs = ch * st.y;   // dS = C P (dPbar - dC) = (C inv) e (dPbar - dC)
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[b][i] = ch * p[b][i] * (dpb[b][i] - dcs);
+      for (int i = 0; i < 4; ++i) p[b][i] = cs * p[b][i] * (dpb[b][i] - dcs);
     BandOperand<T> dso;
     dso.set(p);
     mma_tcontract<T, D>(pend, cur, brow, lo, dso, live, g, n);
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   const T* __restrict__ dO = static_cast<const T*>(a.dO);
   const float* __restrict__ stats = reinterpret_cast<const float*>(a.stats);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, n = lane & 15;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int k0 = tile * BK;
@@ -297,31 +298,25 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  uint32_t live = 0;
-#pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
+  const uint32_t live = live_blocks(mbits);  // wave-uniform
+  const uint32_t full = full_blocks(mbits);
 
-  // Pbar and dPbar of this lane's (key, 4 queries) entries, from the bands:
-  // query block kq + b, key block 7 - b, 16 bytes per block.
-  f32x4 pb[kKeyBlocks], dpb[kKeyBlocks];
-  {
-    const int kq = (k0 >> 4) + w;
-    const int nqb = (a.T + 15) >> 4;
+  // Pbar (phase 0) and dPbar (phase 1) of this lane's (key, 4 queries)
+  // entries, from the bands: query block kq + b, key block 7 - b, 16 bytes
+  // per block; entries beyond the stream or outside the window read as 0.
+  const int kq = (k0 >> 4) + w;
+  const int nqb = (a.T + 15) >> 4;
+  auto band_word = [&](int b) {
+    const int qbk = kq + b < nqb ? kq + b : nqb - 1;
+    return (size_t)qbk * kBandWords + (7 - b) * 256 + n * 16 + 4 * g;
+  };
+  f32x4 pb[kKeyBlocks];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      const int qbk = kq + b < nqb ? kq + b : nqb - 1;  // beyond the stream: masked below
-      const size_t wi = (size_t)qbk * kBandWords + (7 - b) * 256 + n * 16 + 4 * g;
-      const uint4 u = *reinterpret_cast<const uint4*>(a.band + wi);
-      const float4 d4 = *reinterpret_cast<const float4*>(a.dband + wi);
-      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+  for (int b = 0; b < kKeyBlocks; ++b) {
+    const uint4 u = *reinterpret_cast<const uint4*>(a.band + band_word(b));
+    const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool m = (mbits >> (4 * b + i)) & 1u;
-        pb[b][i] = m ? band_decode<T>(uu[i]) : 0.f;
-        dpb[b][i] = m ? dd[i] : 0.f;
-      }
-    }
+    for (int i = 0; i < 4; ++i) pb[b][i] = admitted(mbits, b, i) ? band_decode<T>(uu[i]) : 0.f;
   }
 
   auto rows4 = [&](const float* sc, int field, int b) {
@@ -362,6 +357,12 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   });
 
   // ---- phase 1 (Q_h staged): P_h, dS_h, dK_h = scale dS_h^T Q_h ----
+  f32x4 dpb[kKeyBlocks];
+#pragma unroll
+  for (int b = 0; b < kKeyBlocks; ++b) {
+    const float4 d4 = *reinterpret_cast<const float4*>(a.dband + band_word(b));
+    dpb[b] = f32x4{d4.x, d4.y, d4.z, d4.w};  // only multiplied by P_h, which is 0 where masked
+  }
   RowFrag<T, D> kfb[2];
   load_row_frag<T, D>(kfb[0], k + (size_t)sc_ * H * D, g);
   bool first = true;
@@ -387,12 +388,13 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
       const float4 c4 = rows4(sc, SC_C, b), dc4 = rows4(sc, SC_DC, b);
       const float mxv[4] = {mx.x, mx.y, mx.z, mx.w}, invv[4] = {inv.x, inv.y, inv.z, inv.w};
       const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, dcv[4] = {dc4.x, dc4.y, dc4.z, dc4.w};
+      // dS_h = C P_h (dPbar - dC) with P_h = exp2(s*scale*log2e - max) / sum
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pp =
-            ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(p[b][i] * sl2 - mxv[i]) * invv[i] : 0.f;
-        p[b][i] = cv[i] * pp * (dpb[b][i] - dcv[i]);
-      }
+      for (int i = 0; i < 4; ++i)
+        p[b][i] = (cv[i] * invv[i]) * exp2_scaled(p[b][i], sl2, mxv[i]) * (dpb[b][i] - dcv[i]);
+      if (!((full >> b) & 1u))
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[b][i] = admitted(mbits, b, i) ? p[b][i] : 0.f;
     }
     BandOperand<T> dso;
     dso.set(p);

@@ -93,6 +93,10 @@ struct RowFrag {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Index of this wave in the workgroup, as a wave-uniform (scalar) value, so
+// that addresses derived from it stay in scalar registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -101,6 +105,14 @@ __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp2(s * sl2 - m) with the product rounded before the subtraction (no FMA
+// contraction): when m is the rounded product of the row max, the max entry
+// gets exactly exp2(0) = 1, so a one-key window yields P = 1 exactly.
+__device__ __forceinline__ float exp2_scaled(float s, float sl2, float m) {
+#pragma clang fp contract(off)
+  return __builtin_amdgcn_exp2f(s * sl2 - m);
+}
 
 // Reductions over the four 16-lane groups (lanes n, n+16, n+32, n+48) with
 // the gfx950 lane-swap instructions (VALU only, no LDS round trip):
@@ -134,6 +146,26 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
   return r;
 }
 
+// Wave-uniform bit masks over the 8 token blocks of a wave's band, from the
+// lane's 32 admission bits (bit 4b+i): `live` = some entry admitted, `full` =
+// every entry of every lane admitted (no per-entry masking needed).
+__device__ __forceinline__ uint32_t live_blocks(uint32_t mbits) {
+  uint32_t live = 0;
+#pragma unroll
+  for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
+  return live;
+}
+__device__ __forceinline__ uint32_t full_blocks(uint32_t mbits) {
+  uint32_t full = 0;
+#pragma unroll
+  for (int b = 0; b < kKeyBlocks; ++b)
+    full |= (__all(((mbits >> (4 * b)) & 15u) == 15u) ? 1u : 0u) << b;
+  return full;
+}
+__device__ __forceinline__ bool admitted(uint32_t mbits, int b, int i) {
+  return (mbits >> (4 * b + i)) & 1u;
+}
+
 // ---------------------------------------------------------------------------
 // Buffer resources and DMA staging
 // ---------------------------------------------------------------------------
@@ -162,7 +194,7 @@ __device__ __forceinline__ void issue_tile(T* tile, const T* __restrict__ src, i
   static_assert(R % RPI == 0, "tile rows must fill whole DMA instructions");
   constexpr int NI = R / RPI;
   constexpr int NIW = (NI + NW - 1) / NW;  // instructions per wave
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int lo = row0 > 0 ? row0 : 0;
   const int hi = (row0 + R < T_) ? row0 + R : T_;
   const uint32_t rstride = (uint32_t)H * D * sizeof(T);
@@ -192,7 +224,7 @@ __device__ __forceinline__ void issue_scalars(float* arr, const float* __restric
                                               bool on = true) {
   constexpr int NI = (R + 63) / 64;
   constexpr int NIW = (NI + NW - 1) / NW;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int lo = row0 > 0 ? row0 : 0;
   const int hi = (row0 + R < T_) ? row0 + R : T_;
   const uint32_t rstride = (uint32_t)H * spt * 4u;

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   const T* __restrict__ v = static_cast<const T*>(a.v);
   float* __restrict__ o = a.o;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, n = lane & 15;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int q0 = tile * BQ;
@@ -82,9 +82,8 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  uint32_t live = 0;  // wave-uniform: token blocks with any admitted entry
-#pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
+  const uint32_t live = live_blocks(mbits);  // wave-uniform
+  const uint32_t full = full_blocks(mbits);
 
   const float sl2 = a.scale * kLog2e;
   f32x4 pb[kKeyBlocks];
@@ -130,28 +129,35 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
       sc[b] = zero4();
       if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], cur, brow + 16 * b, lo, qf);
     }
+    // Raw scores; entries outside the window or document become -inf (only
+    // in blocks not fully admitted), so max and exp need no further masking.
+    // The scale is positive, so rounding(s * scale*log2e) is monotonic in s
+    // and the row max of the scaled scores is the scaled raw max: the max
+    // entry gets exp2(0) = 1 exactly (a one-key window gives P = 1).
     float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      if (!((full >> b) & 1u))
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[b][i] *= sl2;
-        if ((mbits >> (4 * b + i)) & 1u) mx = fmaxf(mx, sc[b][i]);
-      }
+        for (int i = 0; i < 4; ++i) sc[b][i] = admitted(mbits, b, i) ? sc[b][i] : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
+    }
     mx = wave_max4(mx);
+    const float mxs = mx == -INFINITY ? 0.f : mx * sl2;  // a row with no key: all terms 0
     float sum = 0.f;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = ((mbits >> (4 * b + i)) & 1u) ? fast_exp2(sc[b][i] - mx) : 0.f;
+        const float e = exp2_scaled(sc[b][i], sl2, mxs);
         sc[b][i] = e;
         sum += e;
       }
     sum = wave_sum4(sum);
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
     const float coef = ch * inv;
-    st_mx = mx;
+    st_mx = mxs;
     st_inv = inv;
     st_h = j;
 #pragma unroll

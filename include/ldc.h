@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   LDC_OK = 0,
   LDC_ERR_NULL = 1,        /* a required pointer is NULL                    */
-  LDC_ERR_SHAPE = 2,       /* T < 0, H < 1, window out of range, overflow   */
+  LDC_ERR_SHAPE = 2,       /* T<0, H<1, window or scale out of range, overflow */
   LDC_ERR_DTYPE = 3,       /* dtype is not an ldc_dtype value               */
   LDC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned              */
   LDC_ERR_UNSUPPORTED = 5, /* head dim not instantiated for this dtype      */
@@ -66,7 +66,8 @@ typedef enum {
 
 /* Forward pass: writes O[T,H,d] in float32.
  * q, k, v: [T,H,d] in `dtype`; c, g: [T,H] float32; doc_ids: [T] int32.
- * scale: the softmax scale (1/sqrt(d) for the textbook choice).
+ * scale: the softmax scale, positive and finite (1/sqrt(d) for the
+ *   textbook choice); other values return LDC_ERR_SHAPE.
  * saved: NULL (inference: nothing saved) or a device buffer of at least
  *   ldc_saved_bytes(...) bytes (16-byte aligned) that receives the state
  *   ldc_bwd needs: the shared map Pbar over each 16-query block's 128-key

@@ -49,21 +49,22 @@ def test_workspace_and_saved_bytes():
     assert ldc.workspace_bytes(ldc.LDC_BF16, 10, 6, 16, 112) == 0  # unsupported -> 0
 
 
-def fwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, saved=None, saved_bytes=0):
+def fwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, saved=None, saved_bytes=0,
+             scale=0.1):
     lib = ldc.load_library()
     p = ptrs or [A] * 7
-    return lib.ldc_fwd(dtype, T, H, d, window, 0.1, *p, saved, saved_bytes, None)
+    return lib.ldc_fwd(dtype, T, H, d, window, scale, *p, saved, saved_bytes, None)
 
 
 def bwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, ws=A, ws_bytes=None,
-             saved=A, saved_bytes=None, entry="ldc_bwd"):
+             saved=A, saved_bytes=None, entry="ldc_bwd", scale=0.1):
     lib = ldc.load_library()
     p = ptrs or [A] * 12
     if ws_bytes is None:
         ws_bytes = ldc.workspace_bytes(dtype, T, H, d, window)
     if saved_bytes is None:
         saved_bytes = ldc.saved_bytes(dtype, T, H, d, window)
-    return getattr(lib, entry)(dtype, T, H, d, window, 0.1, *p[:6], saved, saved_bytes, *p[6:],
+    return getattr(lib, entry)(dtype, T, H, d, window, scale, *p[:6], saved, saved_bytes, *p[6:],
                                ws, ws_bytes, None)
 
 
@@ -83,6 +84,10 @@ def test_validation_errors(call):
     assert call(window=0) == 2
     assert call(window=114) == 2
     assert call(T=1 << 31) == 2                    # too many rows
+    assert call(scale=0.0) == 2                    # scale must be positive and finite
+    assert call(scale=-0.5) == 2
+    assert call(scale=float("inf")) == 2
+    assert call(scale=float("nan")) == 2
     assert call(d=32) == 5                         # LDC_ERR_UNSUPPORTED
     assert call(dtype=ldc.LDC_BF16, d=16) == 5
     nptr = 7 if call is fwd_call else 12
