@@ -88,8 +88,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  const uint32_t live = live_blocks(mbits);  // wave-uniform
-  const uint32_t full = full_blocks(mbits);
+  const uint32_t full = full_blocks(mbits);  // wave-uniform
 
   const float sl2 = a.scale * kLog2e;
   const int qb = (q0 >> 4) + w;         // this wave's 16-query block
@@ -146,17 +145,17 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     const RowFrag<T, D>& df = fb[B];
     const float gh = sb[B];
     float dgs = 0.f;
+    f32x4 bt[kKeyBlocks];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      if (!((live >> b) & 1u)) continue;
-      const f32x4 bt = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, df);
+    for (int b = 0; b < kKeyBlocks; ++b) bt[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, df);
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // masked entries of pb are exactly 0; bt there is finite (zero-filled rows)
-        dgs += pb[b][i] * bt[i];
-        dpb[b][i] += gh * bt[i];
+        dgs += pb[b][i] * bt[b][i];
+        dpb[b][i] += gh * bt[b][i];
       }
-    }
     dg_val = wave_sum4(dgs);
     dg_h = j;
   });
@@ -196,19 +195,23 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     const float2 st = stb[B];  // (row max in log2 units, 1/row sum) saved by the forward pass
     // e = exp2(s*scale*log2e - max) = P_h / inv; masked entries 0
     f32x4 p[kKeyBlocks];
-    float dcs = 0.f;
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      p[b] = zero4();
-      if ((live >> b) & 1u) p[b] = mma_dcontract<T, D>(p[b], cur, brow + 16 * b, lo, qf);
+    for (int b = 0; b < kKeyBlocks; ++b) p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf);
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[b][i] = exp2_scaled(p[b][i], sl2, st.x);  // as in the forward pass
-      if (!((full >> b) & 1u))
+    const uint32_t mb = opaque(mbits), fl = opaque_s(full);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[b][i] = admitted(mbits, b, i) ? p[b][i] : 0.f;
+    for (int b = 0; b < kKeyBlocks; ++b)
+      if (!((fl >> b) & 1u))
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[b][i] = keep_admitted(mb, b, i, p[b][i], 0.f);
+    float dcs = 0.f;
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dcs = fmaf(p[b][i], dpb[b][i], dcs);
-    }
     dcs = wave_sum4(dcs) * st.y;  // dC = sum_s P_h dPbar
     dc_val = dcs;
     const float cs = ch * st.y;   // dS = C P (dPbar - dC) = (C inv) e (dPbar - dC)
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
       for (int i = 0; i < 4; ++i) p[b][i] = cs * p[b][i] * (dpb[b][i] - dcs);
     BandOperand<T> dso;
     dso.set(p);
-    mma_tcontract<T, D>(pend, cur, brow, lo, dso, live, g, n);
+    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n);
     pend_h = j;
   });
   flush_dq();
@@ -298,8 +301,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  const uint32_t live = live_blocks(mbits);  // wave-uniform
-  const uint32_t full = full_blocks(mbits);
+  const uint32_t full = full_blocks(mbits);  // wave-uniform
 
   // Pbar (phase 0) and dPbar (phase 1) of this lane's (key, 4 queries)
   // entries, from the bands: query block kq + b, key block 7 - b, 16 bytes
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     const uint4 u = *reinterpret_cast<const uint4*>(a.band + band_word(b));
     const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pb[b][i] = admitted(mbits, b, i) ? band_decode<T>(uu[i]) : 0.f;
+    for (int i = 0; i < 4; ++i) pb[b][i] = keep_admitted(mbits, b, i, band_decode<T>(uu[i]), 0.f);
   }
 
   auto rows4 = [&](const float* sc, int field, int b) {
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     }
     BandOperand<T> op;
     op.set(gp);
-    mma_tcontract<T, D>(pend, cur, brow, lo, op, live, g, n);
+    mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n);
     pend_h = j;
   });
 
@@ -381,9 +383,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     const RowFrag<T, D>& kf = kfb[B];
     f32x4 p[kKeyBlocks];
 #pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, kf);
+#pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
-      p[b] = zero4();
-      if ((live >> b) & 1u) p[b] = mma_dcontract<T, D>(p[b], cur, brow + 16 * b, lo, kf);
       const float4 mx = rows4(sc, SC_MX, b), inv = rows4(sc, SC_INV, b);
       const float4 c4 = rows4(sc, SC_C, b), dc4 = rows4(sc, SC_DC, b);
       const float mxv[4] = {mx.x, mx.y, mx.z, mx.w}, invv[4] = {inv.x, inv.y, inv.z, inv.w};
@@ -392,13 +394,16 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         p[b][i] = (cv[i] * invv[i]) * exp2_scaled(p[b][i], sl2, mxv[i]) * (dpb[b][i] - dcv[i]);
-      if (!((full >> b) & 1u))
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[b][i] = admitted(mbits, b, i) ? p[b][i] : 0.f;
     }
+    const uint32_t mb = opaque(mbits), fl = opaque_s(full);
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+      if (!((fl >> b) & 1u))
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[b][i] = keep_admitted(mb, b, i, p[b][i], 0.f);
     BandOperand<T> dso;
     dso.set(p);
-    mma_tcontract<T, D>(pend, cur, brow, lo, dso, live, g, n);
+    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n);
     pend_h = j;
   });
   flush(a.dk, a.scale);

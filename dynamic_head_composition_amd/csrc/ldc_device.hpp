@@ -20,6 +20,10 @@
 // chunk c of row r is stored at chunk position c ^ swz(r).  The swizzle makes
 // both read patterns conflict-free: 16 consecutive rows at one chunk (score
 // operands) and 4 consecutive rows x 4 consecutive chunks (transpose reads).
+// A transpose read takes 8-byte halves: in one instruction the lanes reading
+// chunks 4p and 4p+2 take one half and those reading 4p+1 and 4p+3 the other,
+// so that each half-wave (two groups, whose swizzles differ in the lowest
+// chunk bit) touches every bank once.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -146,24 +150,37 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
   return r;
 }
 
-// Wave-uniform bit masks over the 8 token blocks of a wave's band, from the
-// lane's 32 admission bits (bit 4b+i): `live` = some entry admitted, `full` =
-// every entry of every lane admitted (no per-entry masking needed).
-__device__ __forceinline__ uint32_t live_blocks(uint32_t mbits) {
-  uint32_t live = 0;
-#pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) live |= (__any((mbits >> (4 * b)) & 15u) ? 1u : 0u) << b;
-  return live;
-}
+// Wave-uniform bit mask over the 8 token blocks of a wave's band, from the
+// lane's 32 admission bits (bit 4b+i): bit b set when every entry of block b
+// of every lane is admitted (no per-entry masking needed there).
 __device__ __forceinline__ uint32_t full_blocks(uint32_t mbits) {
   uint32_t full = 0;
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b)
     full |= (__all(((mbits >> (4 * b)) & 15u) == 15u) ? 1u : 0u) << b;
+  // one packed scalar, opaque, rather than 8 lane masks kept live for the tests
+  asm volatile("" : "+s"(full));
   return full;
 }
-__device__ __forceinline__ bool admitted(uint32_t mbits, int b, int i) {
-  return (mbits >> (4 * b + i)) & 1u;
+// x where entry (b, i) of the lane's band is admitted, else `other`: a bit
+// select on the lane's admission bits, two vector ALU operations and no
+// per-entry lane masks held in scalar registers.
+__device__ __forceinline__ float keep_admitted(uint32_t mbits, int b, int i, float x, float other) {
+  const int m = (int)(mbits << (31 - (4 * b + i))) >> 31;  // all ones when admitted
+  return __int_as_float((__float_as_int(x) & m) | (__float_as_int(other) & ~m));
+}
+// The value unchanged, but opaque to the optimizer: used once per stage on
+// the admission bits so that the 32 per-entry masks are formed where they are
+// used instead of being hoisted out of the stage loop and kept live.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// The same for a wave-uniform value (the full-block mask): its per-block
+// branch conditions are then scalar bit tests at the point of use.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -277,14 +294,14 @@ struct LaneOffsets {
   static constexpr int ND = Elem<T>::bf16 ? D / 32 : D / 16;  // score-operand reads per row
   static constexpr int NT = Elem<T>::bf16 ? D / 32 : 1;       // transpose-read column groups
   int dk[ND];  // score operand: row n of the block, chunk of k-step kk
-  int tr[NT];  // value operand (bf16): row 4g + n/4, chunk 4p + n%4
+  int tr[NT];  // value operand (bf16): row 4g + n/4, chunk 4p + n%4, half (n/4)%2 (for e = 0)
   __device__ __forceinline__ LaneOffsets(int g, int n) {
     if constexpr (Elem<T>::bf16) {
 #pragma unroll
       for (int kk = 0; kk < ND; ++kk) dk[kk] = n * TL::row_bytes + TL::pos(n, 4 * kk + g) * 16;
       const int rr = n >> 2, bq = n & 3, row = 4 * g + rr;
 #pragma unroll
-      for (int p = 0; p < NT; ++p) tr[p] = row * TL::row_bytes + TL::pos(row, 4 * p + bq) * 16;
+      for (int p = 0; p < NT; ++p) tr[p] = row * TL::row_bytes + TL::pos(row, 4 * p + bq) * 16 + 8 * (bq & 1);
     } else {
 #pragma unroll
       for (int c = 0; c < ND; ++c) dk[c] = n * TL::row_bytes + TL::pos(n, g * (D / 16) + c) * 16;
@@ -355,13 +372,14 @@ struct BandOperand<float> {
 // Contraction over the 128 band tokens:  out[d, n] = sum_tok X[tok, d] * P[tok, n]
 // with X a staged tile (rows base_row + tok) and P the band operand.
 // Result layout (lane: column n; register r = 4*blk + i):
-//   bf16: acc[2p+e][i] <-> d = 32p + 8g + 4e + i  (8 consecutive d per p)
+//   bf16: acc[2p+e][i] <-> d = 32p + 8g + 4(e ^ g%2) + i  (8 consecutive d per p, g)
 //   fp32: acc[db][i]   <-> d = 16db + 4g + i
-// `live` bit b set when token block b holds any admitted pair for this wave.
+// Every token block is contracted (entries outside the band are zero in P):
+// no branches, so the LDS reads of all blocks can be in flight together.
 template <typename T, int D>
 __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* tile, int row16,
                                               const LaneOffsets<T, D>& lo, const BandOperand<T>& P,
-                                              uint32_t live, int g, int n) {
+                                              int g, int n) {
   using TL = Tile<T, D>;
   const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
 #pragma unroll
@@ -370,13 +388,16 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
     typedef __attribute__((address_space(3))) bf16x4 lds_v4;
 #pragma unroll
     for (int ks = 0; ks < kKeyBlocks / 2; ++ks) {
-      if (!((live >> (2 * ks)) & 3u)) continue;
 #pragma unroll
       for (int p = 0; p < D / 32; ++p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          // rows 32ks + 4g + n/4 and 16 further down: same swizzle, immediate offsets
-          const char* a1 = base + lo.tr[p] + 32 * ks * TL::row_bytes + 8 * e;
+          // rows 32ks + 4g + n/4 and 16 further down: same swizzle, immediate
+          // offsets; e flips the 8-byte half the lane reads (recomputed at each
+          // use rather than held in registers across the loop)
+          int off = lo.tr[p];
+          if (e) asm volatile("v_xor_b32 %0, 8, %0" : "+v"(off));
+          const char* a1 = base + off + 32 * ks * TL::row_bytes;
           const char* a2 = a1 + 16 * TL::row_bytes;
           bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
           bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a2));
@@ -389,7 +410,6 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
   } else {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
-      if (!((live >> b) & 1u)) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * b + 4 * g + i;  // relative to row16
@@ -408,7 +428,7 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
 template <typename T>
 __device__ __forceinline__ int tcontract_d(int r, int g) {
   if constexpr (Elem<T>::bf16)
-    return 32 * (r >> 1) + 8 * g + 4 * (r & 1);
+    return 32 * (r >> 1) + 8 * g + 4 * ((r & 1) ^ (g & 1));
   else
     return 16 * r + 4 * g;
 }

@@ -82,8 +82,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  const uint32_t live = live_blocks(mbits);  // wave-uniform
-  const uint32_t full = full_blocks(mbits);
+  const uint32_t full = full_blocks(mbits);  // wave-uniform
 
   const float sl2 = a.scale * kLog2e;
   f32x4 pb[kKeyBlocks];
@@ -125,24 +124,23 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
 
     f32x4 sc[kKeyBlocks];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      sc[b] = zero4();
-      if ((live >> b) & 1u) sc[b] = mma_dcontract<T, D>(sc[b], cur, brow + 16 * b, lo, qf);
-    }
+    for (int b = 0; b < kKeyBlocks; ++b) sc[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf);
     // Raw scores; entries outside the window or document become -inf (only
     // in blocks not fully admitted), so max and exp need no further masking.
     // The scale is positive, so rounding(s * scale*log2e) is monotonic in s
     // and the row max of the scaled scores is the scaled raw max: the max
     // entry gets exp2(0) = 1 exactly (a one-key window gives P = 1).
+    const uint32_t mb = opaque(mbits), fl = opaque_s(full);
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+      if (!((fl >> b) & 1u))
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[b][i] = keep_admitted(mb, b, i, sc[b][i], -INFINITY);
     float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      if (!((full >> b) & 1u))
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[b][i] = admitted(mbits, b, i) ? sc[b][i] : -INFINITY;
+    for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
-    }
     mx = wave_max4(mx);
     const float mxs = mx == -INFINITY ? 0.f : mx * sl2;  // a row with no key: all terms 0
     float sum = 0.f;
@@ -200,7 +198,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     issue_next(1, j, bc);
     if (!real) return;
     const float gh = ghb[B];
-    mma_tcontract<T, D>(pend, cur, brow, lo, pop, live, g, n);
+    mma_tcontract<T, D>(pend, cur, brow, lo, pop, g, n);
 #pragma unroll
     for (int r = 0; r < D / 16; ++r) pend[r] *= gh;
     pend_h = j;
