@@ -120,8 +120,8 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   };
 
   // ---- phase 0 (V_h staged): B_h = dO_h V_h^T, dPbar, dG ----
-  // Small results and output rows are stored at the start of the next stage,
-  // after its barrier, so the stage wait (vmcnt 0) never waits for fresh stores.
+  // Small results are stored at the start of the next stage, after its
+  // barrier, so the stage wait (vmcnt 0) never waits for fresh stores.
   f32x4 dpb[kKeyBlocks];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) dpb[b] = zero4();
@@ -172,11 +172,18 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   f32x4 pend[D / 16];
   float dc_val = 0.f;
   int pend_h = -1;
+  // The previous head's dQ row is stored during this stage's score
+  // contraction, a quarter after every second key block (see mma_tcontract).
+  auto pending = [&]() {
+    return PendingRow{a.dq + ((size_t)t * H + (pend_h >= 0 ? pend_h : 0)) * D, a.scale, pend_h >= 0 && tval};
+  };
+  auto flush_dc = [&]() {
+    if (pend_h >= 0 && tval && g == 0) a.dc[(size_t)t * H + pend_h] = dc_val;
+  };
   auto flush_dq = [&]() {
-    if (pend_h >= 0 && tval) {
-      if (g == 0) a.dc[(size_t)t * H + pend_h] = dc_val;
-      store_row_f32<T, D>(a.dq + ((size_t)t * H + pend_h) * D, pend, a.scale, g);
-    }
+    flush_dc();
+    const PendingRow pr = pending();
+    if (pr.on) store_row_f32<T, D>(pr.row, pend, a.scale, g);
     pend_h = -1;
   };
   preload(q, a.c, true);
@@ -186,27 +193,29 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     wait_dma();
     const bool real = j < H;
     prefetch(j, bc, q, a.c, true);
-    flush_dq();
+    flush_dc();
     __builtin_amdgcn_sched_barrier(0);
     issue_next(1, j, bc);
-    if (!real) return;
+    if (!real) {
+      flush_dq();
+      return;
+    }
+    const PendingRow prev = pending();
     const RowFrag<T, D>& qf = fb[B];
     const float ch = sb[B];
     const float2 st = stb[B];  // (row max in log2 units, 1/row sum) saved by the forward pass
     // e = exp2(s*scale*log2e - max) = P_h / inv; masked entries 0
     f32x4 p[kKeyBlocks];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf);
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf);
+      if (b & 1) store_pending_chunk<T, D>(prev, pend, g, b >> 1);
+    }
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[b][i] = exp2_scaled(p[b][i], sl2, st.x);  // as in the forward pass
-    const uint32_t mb = opaque(mbits), fl = opaque_s(full);
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-      if (!((fl >> b) & 1u))
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[b][i] = keep_admitted(mb, b, i, p[b][i], 0.f);
+    mask_band(p, mbits, full, 0.f);
     float dcs = 0.f;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
       for (int i = 0; i < 4; ++i) p[b][i] = cs * p[b][i] * (dpb[b][i] - dcs);
     BandOperand<T> dso;
     dso.set(p);
-    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n);
+    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, PendingRow{nullptr, 0.f, false});
     pend_h = j;
   });
   flush_dq();
@@ -326,12 +335,16 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   };
   const float sl2 = a.scale * kLog2e;
 
-  // A stage's output row is stored at the start of the next stage, after its
-  // barrier: the stage wait (vmcnt 0) then never waits for fresh stores.
+  // A stage's output row is stored during the next stage, after that stage's
+  // DMA has been issued, spread over its contractions (see mma_tcontract).
   f32x4 pend[D / 16];
   int pend_h = -1;
+  auto pending = [&](float* dst, float scale) {
+    return PendingRow{dst + ((size_t)s * H + (pend_h >= 0 ? pend_h : 0)) * D, scale, pend_h >= 0 && sval};
+  };
   auto flush = [&](float* dst, float scale) {
-    if (pend_h >= 0 && sval) store_row_f32<T, D>(dst + ((size_t)s * H + pend_h) * D, pend, scale, g);
+    const PendingRow pr = pending(dst, scale);
+    if (pr.on) store_row_f32<T, D>(pr.row, pend, scale, g);
     pend_h = -1;
   };
 
@@ -342,10 +355,12 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     const float* sc = B == 0 ? s_sc0 : s_sc1;
     wait_dma();
     const bool real = j < H;
-    flush(a.dv, 1.f);
     __builtin_amdgcn_sched_barrier(0);
     issue_next(0, j, bc);
-    if (!real) return;
+    if (!real) {
+      flush(a.dv, 1.f);
+      return;
+    }
     f32x4 gp[kKeyBlocks];
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
@@ -354,7 +369,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     }
     BandOperand<T> op;
     op.set(gp);
-    mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n);
+    mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n, pending(a.dv, 1.f));
     pend_h = j;
   });
 
@@ -375,15 +390,23 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     wait_dma();
     const bool real = j < H;
     load_row_frag<T, D>(kfb[1 - B], k + ((size_t)sc_ * H + (j + 1 < H ? j + 1 : 0)) * D, g);
-    flush(first ? a.dv : a.dk, first ? 1.f : a.scale);
+    // the first stage of this phase stores the last dV row
+    const PendingRow prev = pending(first ? a.dv : a.dk, first ? 1.f : a.scale);
     first = false;
     __builtin_amdgcn_sched_barrier(0);
     issue_next(1, j, bc);
-    if (!real) return;
+    if (!real) {
+      if (prev.on) store_row_f32<T, D>(prev.row, pend, prev.scale, g);
+      pend_h = -1;
+      return;
+    }
     const RowFrag<T, D>& kf = kfb[B];
     f32x4 p[kKeyBlocks];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, kf);
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, kf);
+      if (b & 1) store_pending_chunk<T, D>(prev, pend, g, b >> 1);
+    }
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       const float4 mx = rows4(sc, SC_MX, b), inv = rows4(sc, SC_INV, b);
@@ -395,15 +418,10 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
       for (int i = 0; i < 4; ++i)
         p[b][i] = (cv[i] * invv[i]) * exp2_scaled(p[b][i], sl2, mxv[i]) * (dpb[b][i] - dcv[i]);
     }
-    const uint32_t mb = opaque(mbits), fl = opaque_s(full);
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-      if (!((fl >> b) & 1u))
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[b][i] = keep_admitted(mb, b, i, p[b][i], 0.f);
+    mask_band(p, mbits, full, 0.f);
     BandOperand<T> dso;
     dso.set(p);
-    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n);
+    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, PendingRow{nullptr, 0.f, false});
     pend_h = j;
   });
   flush(a.dk, a.scale);

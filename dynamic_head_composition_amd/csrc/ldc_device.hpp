@@ -36,6 +36,9 @@ namespace ldc {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // storage of one bfloat16
 typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
@@ -142,14 +145,6 @@ __device__ __forceinline__ float swap32_sum(float x) {
 __device__ __forceinline__ float wave_max4(float x) { return swap32_max(swap16_max(x)); }
 __device__ __forceinline__ float wave_sum4(float x) { return swap32_sum(swap16_sum(x)); }
 
-__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float b0, float b1,
-                                        float b2, float b3) {
-  bf16x8 r;
-  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
-  r[4] = (__bf16)b0; r[5] = (__bf16)b1; r[6] = (__bf16)b2; r[7] = (__bf16)b3;
-  return r;
-}
-
 // Wave-uniform bit mask over the 8 token blocks of a wave's band, from the
 // lane's 32 admission bits (bit 4b+i): bit b set when every entry of block b
 // of every lane is admitted (no per-entry masking needed there).
@@ -183,6 +178,29 @@ __device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
   return x;
 }
 
+// Replace the entries of a lane's band that are not admitted by `other`.
+// In a wave whose band lies inside one document, only the first and the last
+// token blocks are partial (the window's far edge and the causal diagonal);
+// that case takes a branch of its own, the general case tests every block.
+__device__ __forceinline__ void mask_band(f32x4 (&p)[kKeyBlocks], uint32_t mbits, uint32_t full,
+                                          float other) {
+  constexpr uint32_t kInner = ((1u << kKeyBlocks) - 1) & ~1u & ~(1u << (kKeyBlocks - 1));
+  const uint32_t mb = opaque(mbits), fl = opaque_s(full);
+  if (fl == kInner) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[0][i] = keep_admitted(mb, 0, i, p[0][i], other);
+      p[kKeyBlocks - 1][i] = keep_admitted(mb, kKeyBlocks - 1, i, p[kKeyBlocks - 1][i], other);
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+      if (!((fl >> b) & 1u))
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[b][i] = keep_admitted(mb, b, i, p[b][i], other);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Buffer resources and DMA staging
 // ---------------------------------------------------------------------------
@@ -203,7 +221,9 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // one: identical bytes to identical LDS addresses), so that the compiler's
 // wait counters see one straight-line sequence of vector-memory operations.
 // Completion is waited for with s_waitcnt vmcnt + a barrier by the caller.
-template <typename T, int D, int R, int NW>
+// Instructions [U0, U1) of the wave's sequence only, when the issue is spread
+// over a stage.
+template <typename T, int D, int R, int NW, int U0 = 0, int U1 = 1 << 20>
 __device__ __forceinline__ void issue_tile(T* tile, const T* __restrict__ src, int row0, int T_,
                                            int H, int h, bool on = true) {
   using TL = Tile<T, D>;
@@ -221,7 +241,7 @@ __device__ __forceinline__ void issue_tile(T* tile, const T* __restrict__ src, i
   const int rsub = lane / TL::chunks, pc = lane % TL::chunks;
   char* base = reinterpret_cast<char*>(tile);
 #pragma unroll
-  for (int u = 0; u < NIW; ++u) {
+  for (int u = U0; u < (U1 < NIW ? U1 : NIW); ++u) {
     const int j = (w + u * NW < NI) ? w + u * NW : NI - 1;
     const int rl = j * RPI + rsub;
     const int s = row0 + rl;
@@ -350,14 +370,23 @@ struct BandOperand<bf16_t> {
   bf16x8 hi[kKeyBlocks / 2], lo[kKeyBlocks / 2];
   __device__ __forceinline__ void set(const f32x4 (&p)[kKeyBlocks]) {
 #pragma unroll
-    for (int ks = 0; ks < kKeyBlocks / 2; ++ks)
+    for (int ks = 0; ks < kKeyBlocks / 2; ++ks) {
+      u32x4 h4, l4;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = p[2 * ks + (j >> 2)][j & 3];
-        const __bf16 h = (__bf16)x;
-        hi[ks][j] = h;
-        lo[ks][j] = (__bf16)(x - (float)h);
+      for (int jp = 0; jp < 4; ++jp) {
+        // slots 2jp, 2jp+1: one packed conversion for the pair, the high
+        // parts widened back by shifts, one packed conversion of the remainders
+        const float x0 = p[2 * ks + (jp >> 1)][2 * (jp & 1)];
+        const float x1 = p[2 * ks + (jp >> 1)][2 * (jp & 1) + 1];
+        const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+        const float r0 = x0 - __uint_as_float(hb << 16);
+        const float r1 = x1 - __uint_as_float(hb & 0xffff0000u);
+        h4[jp] = hb;
+        l4[jp] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
       }
+      hi[ks] = __builtin_bit_cast(bf16x8, h4);
+      lo[ks] = __builtin_bit_cast(bf16x8, l4);
+    }
   }
 };
 template <>
@@ -369,62 +398,8 @@ struct BandOperand<float> {
   }
 };
 
-// Contraction over the 128 band tokens:  out[d, n] = sum_tok X[tok, d] * P[tok, n]
-// with X a staged tile (rows base_row + tok) and P the band operand.
-// Result layout (lane: column n; register r = 4*blk + i):
-//   bf16: acc[2p+e][i] <-> d = 32p + 8g + 4(e ^ g%2) + i  (8 consecutive d per p, g)
-//   fp32: acc[db][i]   <-> d = 16db + 4g + i
-// Every token block is contracted (entries outside the band are zero in P):
-// no branches, so the LDS reads of all blocks can be in flight together.
-template <typename T, int D>
-__device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* tile, int row16,
-                                              const LaneOffsets<T, D>& lo, const BandOperand<T>& P,
-                                              int g, int n) {
-  using TL = Tile<T, D>;
-  const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
-#pragma unroll
-  for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
-  if constexpr (Elem<T>::bf16) {
-    typedef __attribute__((address_space(3))) bf16x4 lds_v4;
-#pragma unroll
-    for (int ks = 0; ks < kKeyBlocks / 2; ++ks) {
-#pragma unroll
-      for (int p = 0; p < D / 32; ++p) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          // rows 32ks + 4g + n/4 and 16 further down: same swizzle, immediate
-          // offsets; e flips the 8-byte half the lane reads (recomputed at each
-          // use rather than held in registers across the loop)
-          int off = lo.tr[p];
-          if (e) asm volatile("v_xor_b32 %0, 8, %0" : "+v"(off));
-          const char* a1 = base + off + 32 * ks * TL::row_bytes;
-          const char* a2 = a1 + 16 * TL::row_bytes;
-          bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
-          bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a2));
-          bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[2 * p + e] = mma(a, P.hi[ks], acc[2 * p + e]);
-          acc[2 * p + e] = mma(a, P.lo[ks], acc[2 * p + e]);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * b + 4 * g + i;  // relative to row16
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          const float x = *reinterpret_cast<const float*>(base + TL::off(r, 16 * db + n));
-          acc[db] = mma(x, P.v[b][i], acc[db]);
-        }
-      }
-    }
-  }
-}
-
 // Offset (elements) of the 4 consecutive d-values a lane holds in acc[r] of
-// mma_tcontract's result (the lane's group g).
+// mma_tcontract's result (the lane's group g; layout given there).
 template <typename T>
 __device__ __forceinline__ int tcontract_d(int r, int g) {
   if constexpr (Elem<T>::bf16)
@@ -443,6 +418,104 @@ __device__ __forceinline__ void store_row_f32(float* __restrict__ row, const f32
                                               float s, int g) {
 #pragma unroll
   for (int r = 0; r < D / 16; ++r) store4(row + tcontract_d<T>(r, g), acc[r], s);
+}
+
+// A finished output row still held in registers, to be stored while the next
+// result is computed (`on` per lane: rows past the stream are not stored).
+struct PendingRow {
+  float* row;
+  float scale;
+  bool on;
+};
+
+// Keep vector-memory writes from being moved across this point by the
+// scheduler; every other kind of instruction may still move across it.
+__device__ __forceinline__ void store_fence() { __builtin_amdgcn_sched_barrier(0x00A1); }
+
+// Store chunk c of 4 of a pending row (D/64 registers each; all of it from
+// chunk 0 when D < 64), for callers that spread the stores over a loop.
+template <typename T, int D>
+__device__ __forceinline__ void store_pending_chunk(const PendingRow& prev, const f32x4 (&acc)[D / 16],
+                                                    int g, int c) {
+  constexpr int NR = D / 16, NC = NR < 4 ? 1 : 4, RPC = NR / NC;
+  if (c < NC && prev.on)
+#pragma unroll
+    for (int r = c * RPC; r < (c + 1) * RPC; ++r) store4(prev.row + tcontract_d<T>(r, g), acc[r], prev.scale);
+  store_fence();
+}
+
+// Contraction over the 128 band tokens:  out[d, n] = sum_tok X[tok, d] * P[tok, n]
+// with X a staged tile (rows base_row + tok) and P the band operand.
+// Result layout (lane: column n; register r = 4*blk + i):
+//   bf16: acc[2p+e][i] <-> d = 32p + 8g + 4(e ^ g%2) + i  (8 consecutive d per p, g)
+//   fp32: acc[db][i]   <-> d = 16db + 4g + i
+// Every token block is contracted (entries outside the band are zero in P):
+// no branches, so the LDS reads of all blocks can be in flight together.
+// If prev.on, acc holds the previous result row on entry; it is stored group
+// by group just before the group's registers are reused, so the stores leave
+// spread over the contraction instead of in one burst (a burst of stores
+// stalls the wave until the memory pipeline has taken them).
+template <typename T, int D>
+__device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* tile, int row16,
+                                              const LaneOffsets<T, D>& lo, const BandOperand<T>& P,
+                                              int g, int n, const PendingRow& prev) {
+  using TL = Tile<T, D>;
+  const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
+  if constexpr (Elem<T>::bf16) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+    constexpr int NP = D / 32;            // column groups of 32
+    constexpr int PG = NP >= 4 ? 2 : 1;   // column groups per store group
+#pragma unroll
+    for (int p0 = 0; p0 < NP; p0 += PG) {
+      if (prev.on)
+#pragma unroll
+        for (int r = 2 * p0; r < 2 * (p0 + PG); ++r)
+          store4(prev.row + tcontract_d<T>(r, g), acc[r], prev.scale);
+      store_fence();
+#pragma unroll
+      for (int r = 2 * p0; r < 2 * (p0 + PG); ++r) acc[r] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < kKeyBlocks / 2; ++ks) {
+#pragma unroll
+        for (int p = p0; p < p0 + PG; ++p) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            // rows 32ks + 4g + n/4 and 16 further down: same swizzle, immediate
+            // offsets; e flips the 8-byte half the lane reads (recomputed at
+            // each use rather than held in registers across the loop)
+            int off = lo.tr[p];
+            if (e) asm volatile("v_xor_b32 %0, 8, %0" : "+v"(off));
+            const char* a1 = base + off + 32 * ks * TL::row_bytes;
+            const char* a2 = a1 + 16 * TL::row_bytes;
+            bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
+            bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a2));
+            bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[2 * p + e] = mma(a, P.hi[ks], acc[2 * p + e]);
+            acc[2 * p + e] = mma(a, P.lo[ks], acc[2 * p + e]);
+          }
+        }
+      }
+    }
+  } else {
+    if (prev.on)
+#pragma unroll
+      for (int r = 0; r < D / 16; ++r) store4(prev.row + tcontract_d<T>(r, g), acc[r], prev.scale);
+    store_fence();
+#pragma unroll
+    for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * b + 4 * g + i;  // relative to row16
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const float x = *reinterpret_cast<const float*>(base + TL::off(r, 16 * db + n));
+          acc[db] = mma(x, P.v[b][i], acc[db]);
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

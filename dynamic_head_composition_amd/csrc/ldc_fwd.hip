@@ -130,12 +130,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     // The scale is positive, so rounding(s * scale*log2e) is monotonic in s
     // and the row max of the scaled scores is the scaled raw max: the max
     // entry gets exp2(0) = 1 exactly (a one-key window gives P = 1).
-    const uint32_t mb = opaque(mbits), fl = opaque_s(full);
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-      if (!((fl >> b) & 1u))
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[b][i] = keep_admitted(mb, b, i, sc[b][i], -INFINITY);
+    mask_band(sc, mbits, full, -INFINITY);
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
@@ -177,14 +172,18 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   }
 
   // ---- phase 1 (V_h staged): O^T_h = V_h^T Pbar^T, scaled by G ----
-  // A stage's output row is stored at the start of the next stage, after its
-  // barrier: the stage wait (vmcnt 0) then never waits for fresh stores.
+  // A stage's output row is stored during the next stage, spread over its
+  // contraction, after that stage's DMA has been issued.
   float ghb[2];
   ghb[0] = a.g[(size_t)tc * H];
   f32x4 pend[D / 16];
   int pend_h = -1;
+  auto pending = [&]() {
+    return PendingRow{o + ((size_t)t * H + (pend_h >= 0 ? pend_h : 0)) * D, 1.f, pend_h >= 0 && tval};
+  };
   auto flush = [&]() {
-    if (pend_h >= 0 && tval) store_row_f32<T, D>(o + ((size_t)t * H + pend_h) * D, pend, 1.f, g);
+    const PendingRow pr = pending();
+    if (pr.on) store_row_f32<T, D>(pr.row, pend, 1.f, g);
     pend_h = -1;
   };
   for_stage_pairs(Hp, [&](int j, auto bc) {
@@ -193,12 +192,14 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     wait_dma();
     const bool real = j < H;
     ghb[1 - B] = a.g[(size_t)tc * H + (j + 1 < H ? j + 1 : 0)];
-    flush();
     __builtin_amdgcn_sched_barrier(0);
     issue_next(1, j, bc);
-    if (!real) return;
+    if (!real) {
+      flush();
+      return;
+    }
     const float gh = ghb[B];
-    mma_tcontract<T, D>(pend, cur, brow, lo, pop, g, n);
+    mma_tcontract<T, D>(pend, cur, brow, lo, pop, g, n, pending());
 #pragma unroll
     for (int r = 0; r < D / 16; ++r) pend[r] *= gh;
     pend_h = j;
