@@ -172,8 +172,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   f32x4 pend[D / 16];
   float dc_val = 0.f;
   int pend_h = -1;
-  // The previous head's dQ row is stored during this stage's score
-  // contraction, a quarter after every second key block (see mma_tcontract).
+  // The previous head's dQ row is stored during this stage's token
+  // contraction (see mma_tcontract), late in the stage: stores issued early
+  // would queue ahead of the other waves' DMA of the next tile.
   auto pending = [&]() {
     return PendingRow{a.dq + ((size_t)t * H + (pend_h >= 0 ? pend_h : 0)) * D, a.scale, pend_h >= 0 && tval};
   };
@@ -209,7 +210,6 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf);
-      if (b & 1) store_pending_chunk<T, D>(prev, pend, g, b >> 1);
     }
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
       for (int i = 0; i < 4; ++i) p[b][i] = cs * p[b][i] * (dpb[b][i] - dcs);
     BandOperand<T> dso;
     dso.set(p);
-    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, PendingRow{nullptr, 0.f, false});
+    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, prev);
     pend_h = j;
   });
   flush_dq();
@@ -390,7 +390,8 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     wait_dma();
     const bool real = j < H;
     load_row_frag<T, D>(kfb[1 - B], k + ((size_t)sc_ * H + (j + 1 < H ? j + 1 : 0)) * D, g);
-    // the first stage of this phase stores the last dV row
+    // the first stage of this phase stores the last dV row (during its token
+    // contraction, late in the stage: see the query-side kernel)
     const PendingRow prev = pending(first ? a.dv : a.dk, first ? 1.f : a.scale);
     first = false;
     __builtin_amdgcn_sched_barrier(0);
@@ -405,7 +406,6 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, kf);
-      if (b & 1) store_pending_chunk<T, D>(prev, pend, g, b >> 1);
     }
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     mask_band(p, mbits, full, 0.f);
     BandOperand<T> dso;
     dso.set(p);
-    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, PendingRow{nullptr, 0.f, false});
+    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, prev);
     pend_h = j;
   });
   flush(a.dk, a.scale);

@@ -432,18 +432,6 @@ struct PendingRow {
 // scheduler; every other kind of instruction may still move across it.
 __device__ __forceinline__ void store_fence() { __builtin_amdgcn_sched_barrier(0x00A1); }
 
-// Store chunk c of 4 of a pending row (D/64 registers each; all of it from
-// chunk 0 when D < 64), for callers that spread the stores over a loop.
-template <typename T, int D>
-__device__ __forceinline__ void store_pending_chunk(const PendingRow& prev, const f32x4 (&acc)[D / 16],
-                                                    int g, int c) {
-  constexpr int NR = D / 16, NC = NR < 4 ? 1 : 4, RPC = NR / NC;
-  if (c < NC && prev.on)
-#pragma unroll
-    for (int r = c * RPC; r < (c + 1) * RPC; ++r) store4(prev.row + tcontract_d<T>(r, g), acc[r], prev.scale);
-  store_fence();
-}
-
 // Contraction over the 128 band tokens:  out[d, n] = sum_tok X[tok, d] * P[tok, n]
 // with X a staged tile (rows base_row + tok) and P the band operand.
 // Result layout (lane: column n; register r = 4*blk + i):
