@@ -40,6 +40,12 @@ SMALL = [  # (T, H, d, dtype, window, docs, seed)
     (1000, 12, 64, "bf16", 112, ("uniform", 8, 256), 7),
     (333, 6, 128, "bf16", 37, ("geometric", 100), 8),
     (129, 2, 64, "bf16", 112, ("single",), 9),
+    # odd head counts (a padding stage closes each phase), the widest window
+    (500, 3, 128, "bf16", 113, ("geometric", 150), 20),
+    (400, 5, 64, "bf16", 100, ("uniform", 8, 64), 21),
+    # a whole number of 128-token tiles; several tiles per XCD
+    (256, 6, 128, "bf16", 112, ("single",), 22),
+    (4096, 6, 128, "bf16", 112, ("geometric", 1024), 23),
 ]
 
 
@@ -166,3 +172,46 @@ def test_autograd_function(ldc):
     gr = orc.backward(w.q, w.k, w.v, w.c, w.g, w.doc, w.do, window=w.window, scale=w.scale)
     for name, ref in zip(("q", "k", "v", "c", "g"), gr):
         assert_close("d" + name, to_np(ts[name].grad), ref, "f32")
+
+
+def test_split_backward_matches(ldc):
+    """ldc_bwd_q then ldc_bwd_kv on one workspace gives exactly ldc_bwd."""
+    import torch
+    w = wl.make_workload(700, 6, 128, dtype="bf16", seed=24)
+    x = w.torch_inputs("cuda", with_do=True)
+    args = (x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"])
+    _, saved = ldc.fwd(*args, window=w.window, scale=w.scale, save=True)
+    full = ldc.bwd(*args, saved, x["do"], window=w.window, scale=w.scale)
+    ws = torch.empty(ldc.workspace_bytes(ldc.LDC_BF16, 700, 6, 128, w.window), dtype=torch.uint8,
+                     device="cuda")
+    outs = tuple(torch.empty_like(t) for t in full)
+    ldc.bwd(*args, saved, x["do"], window=w.window, scale=w.scale, out=outs, workspace=ws, part="q")
+    ldc.bwd(*args, saved, x["do"], window=w.window, scale=w.scale, out=outs, workspace=ws, part="kv")
+    torch.cuda.synchronize()
+    for name, a_, b_ in zip(GRADS, full, outs):
+        assert torch.equal(a_, b_), name
+
+
+def test_custom_scale(ldc):
+    """A softmax scale other than 1/sqrt(d) is honoured by both passes."""
+    w = wl.make_workload(300, 2, 128, dtype="bf16", seed=25, scale=0.37)
+    check_all(ldc, w)
+
+
+def test_side_stream(ldc):
+    """Work enqueued on a non-default stream gives the default-stream result."""
+    import torch
+    w = wl.make_workload(600, 6, 128, dtype="bf16", seed=26)
+    ref, _ = run_gpu(ldc, w)
+    x = w.torch_inputs("cuda", with_do=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, saved = ldc.fwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], window=w.window,
+                           scale=w.scale, save=True)
+        grads = ldc.bwd(x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"], saved, x["do"],
+                        window=w.window, scale=w.scale)
+    s.synchronize()
+    assert torch.equal(o, ref["o"])
+    for name, gr in zip(GRADS, grads):
+        assert torch.equal(gr, ref[name]), name
