@@ -64,9 +64,18 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     T* buf = decltype(bc)::value == 0 ? s_x0 : s_x1;
     issue_tile<T, D, R, NW>(buf, phase == 0 ? v : k, span0, a.T, H, h, on);
   };
-  auto issue_next = [&](int phase, int j, auto bc) {
+  // part pp of the DMA of the stage after stage j of `phase`
+  auto issue_part = [&](int phase, int j, auto bc, auto pp) {
+    constexpr int NIW = tile_insts_per_wave<T, D, R, NW>(), P = decltype(pp)::value;
     const NextStage ns = next_stage(phase, j, H, Hp, 2);
-    issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<1 - decltype(bc)::value>{});
+    T* buf = decltype(bc)::value == 0 ? s_x1 : s_x0;
+    __builtin_amdgcn_sched_barrier(0);
+    issue_tile<T, D, R, NW, P * NIW / kIssueParts, (P + 1) * NIW / kIssueParts>(
+        buf, ns.phase == 0 ? v : k, span0, a.T, H, ns.head >= 0 ? ns.head : 0, ns.head >= 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto issue_rest = [&](int phase, int j, auto bc, auto from) {
+    static_for<decltype(from)::value, kIssueParts>([&](auto pp) { issue_part(phase, j, bc, pp); });
   };
   issue(0, 0, true, Buf<0>{});
 
@@ -139,15 +148,22 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     const bool real = j < H;
     prefetch(j, bc, dO, a.g, false);
     flush_dg();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_next(0, j, bc);
-    if (!real) return;
+    issue_part(0, j, bc, Part<0>{});
+    if (!real) {
+      issue_rest(0, j, bc, Part<1>{});
+      return;
+    }
     const RowFrag<T, D>& df = fb[B];
     const float gh = sb[B];
     float dgs = 0.f;
     f32x4 bt[kKeyBlocks];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) bt[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, df);
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      bt[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, df);
+      if (b == 1) issue_part(0, j, bc, Part<1>{});
+      if (b == 3) issue_part(0, j, bc, Part<2>{});
+      if (b == 5) issue_part(0, j, bc, Part<3>{});
+    }
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
@@ -195,9 +211,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     const bool real = j < H;
     prefetch(j, bc, q, a.c, true);
     flush_dc();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_next(1, j, bc);
+    issue_part(1, j, bc, Part<0>{});
     if (!real) {
+      issue_rest(1, j, bc, Part<1>{});
       flush_dq();
       return;
     }
@@ -210,6 +226,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf);
+      if (b == 1) issue_part(1, j, bc, Part<1>{});
+      if (b == 3) issue_part(1, j, bc, Part<2>{});
+      if (b == 5) issue_part(1, j, bc, Part<3>{});
     }
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
@@ -286,9 +305,29 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     issue_scalars<R, NW>(sc + SC_MX * RP, stats, 2, 0, span0, a.T, H, h, on);
     issue_scalars<R, NW>(sc + SC_INV * RP, stats, 2, 1, span0, a.T, H, h, on);
   };
-  auto issue_next = [&](int phase, int j, auto bc) {
+  // part pp of the DMA of the stage after stage j of `phase` (part 0 also
+  // issues the per-row scalars)
+  auto issue_part = [&](int phase, int j, auto bc, auto pp) {
+    constexpr int NIW = tile_insts_per_wave<T, D, R, NW>(), P = decltype(pp)::value;
     const NextStage ns = next_stage(phase, j, H, Hp, 2);
-    issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<1 - decltype(bc)::value>{});
+    const int h = ns.head >= 0 ? ns.head : 0;
+    const bool on = ns.head >= 0;
+    T* buf = decltype(bc)::value == 0 ? s_x1 : s_x0;
+    float* sc = decltype(bc)::value == 0 ? s_sc1 : s_sc0;
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (P == 0) {
+      issue_scalars<R, NW>(sc + SC_C * RP, a.c, 1, 0, span0, a.T, H, h, on);
+      issue_scalars<R, NW>(sc + SC_G * RP, a.g, 1, 0, span0, a.T, H, h, on);
+      issue_scalars<R, NW>(sc + SC_DC * RP, a.dc, 1, 0, span0, a.T, H, h, on);
+      issue_scalars<R, NW>(sc + SC_MX * RP, stats, 2, 0, span0, a.T, H, h, on);
+      issue_scalars<R, NW>(sc + SC_INV * RP, stats, 2, 1, span0, a.T, H, h, on);
+    }
+    issue_tile<T, D, R, NW, P * NIW / kIssueParts, (P + 1) * NIW / kIssueParts>(
+        buf, ns.phase == 0 ? dO : q, span0, a.T, H, h, on);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto issue_rest = [&](int phase, int j, auto bc, auto from) {
+    static_for<decltype(from)::value, kIssueParts>([&](auto pp) { issue_part(phase, j, bc, pp); });
   };
   issue(0, 0, true, Buf<0>{});
 
@@ -355,9 +394,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     const float* sc = B == 0 ? s_sc0 : s_sc1;
     wait_dma();
     const bool real = j < H;
-    __builtin_amdgcn_sched_barrier(0);
-    issue_next(0, j, bc);
+    issue_part(0, j, bc, Part<0>{});
     if (!real) {
+      issue_rest(0, j, bc, Part<1>{});
       flush(a.dv, 1.f);
       return;
     }
@@ -369,7 +408,10 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     }
     BandOperand<T> op;
     op.set(gp);
-    mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n, pending(a.dv, 1.f));
+    mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n, pending(a.dv, 1.f), [&](auto pp) {
+      if constexpr (decltype(pp)::value < kIssueParts) issue_part(0, j, bc, pp);
+    });
+    issue_rest(0, j, bc, Part<tcontract_groups<T, D>()>{});
     pend_h = j;
   });
 
@@ -394,9 +436,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     // contraction, late in the stage: see the query-side kernel)
     const PendingRow prev = pending(first ? a.dv : a.dk, first ? 1.f : a.scale);
     first = false;
-    __builtin_amdgcn_sched_barrier(0);
-    issue_next(1, j, bc);
+    issue_part(1, j, bc, Part<0>{});
     if (!real) {
+      issue_rest(1, j, bc, Part<1>{});
       if (prev.on) store_row_f32<T, D>(prev.row, pend, prev.scale, g);
       pend_h = -1;
       return;
@@ -406,6 +448,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, kf);
+      if (b == 1) issue_part(1, j, bc, Part<1>{});
+      if (b == 3) issue_part(1, j, bc, Part<2>{});
+      if (b == 5) issue_part(1, j, bc, Part<3>{});
     }
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {

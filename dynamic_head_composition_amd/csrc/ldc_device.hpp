@@ -50,6 +50,15 @@ constexpr int kHalo = kBand - 16;             // 112 rows before a 16-row block
 constexpr int kMaxWindow = kHalo + 1;         // 113: widest window the band holds
 constexpr float kLog2e = 1.4426950408889634f;
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Direct global -> LDS load through a buffer resource (llvm.amdgcn.raw.buffer.load.lds).
 extern "C" __device__ void ldc_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
                                                int soffset, int offset,
@@ -221,8 +230,14 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // one: identical bytes to identical LDS addresses), so that the compiler's
 // wait counters see one straight-line sequence of vector-memory operations.
 // Completion is waited for with s_waitcnt vmcnt + a barrier by the caller.
-// Instructions [U0, U1) of the wave's sequence only, when the issue is spread
-// over a stage.
+// Instructions each wave issues for one tile (the issue_tile sequence length).
+template <typename T, int D, int R, int NW>
+constexpr int tile_insts_per_wave() {
+  return (R / Tile<T, D>::rows_per_inst + NW - 1) / NW;
+}
+
+// With U0/U1, only instructions [U0, U1) of the wave's sequence are issued
+// (for callers that spread the issue over a stage).
 template <typename T, int D, int R, int NW, int U0 = 0, int U1 = 1 << 20>
 __device__ __forceinline__ void issue_tile(T* tile, const T* __restrict__ src, int row0, int T_,
                                            int H, int h, bool on = true) {
@@ -443,18 +458,33 @@ __device__ __forceinline__ void store_fence() { __builtin_amdgcn_sched_barrier(0
 // by group just before the group's registers are reused, so the stores leave
 // spread over the contraction instead of in one burst (a burst of stores
 // stalls the wave until the memory pipeline has taken them).
+// hook(Part<k>) runs before column group k >= 1 (bf16; k < tcontract_groups),
+// so that callers can spread other work (the next stage's DMA) over the
+// contraction.
+template <int P>
+using Part = std::integral_constant<int, P>;
 template <typename T, int D>
+constexpr int tcontract_groups() {
+  return Elem<T>::bf16 ? D / 32 : 1;
+}
+struct NoHook {
+  template <typename P>
+  __device__ __forceinline__ void operator()(P) const {}
+};
+template <typename T, int D, typename Hook = NoHook>
 __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* tile, int row16,
                                               const LaneOffsets<T, D>& lo, const BandOperand<T>& P,
-                                              int g, int n, const PendingRow& prev) {
+                                              int g, int n, const PendingRow& prev,
+                                              Hook&& hook = Hook{}) {
   using TL = Tile<T, D>;
   const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
   if constexpr (Elem<T>::bf16) {
     typedef __attribute__((address_space(3))) bf16x4 lds_v4;
-    constexpr int NP = D / 32;            // column groups of 32
-    constexpr int PG = NP >= 4 ? 2 : 1;   // column groups per store group
-#pragma unroll
-    for (int p0 = 0; p0 < NP; p0 += PG) {
+    constexpr int NP = D / 32;  // column groups of 32
+    constexpr int PG = 1;       // column groups per store group
+    static_for<0, NP / PG>([&](auto gi) {
+      constexpr int p0 = decltype(gi)::value * PG;
+      if constexpr (p0 > 0) hook(Part<p0 / PG>{});
       if (prev.on)
 #pragma unroll
         for (int r = 2 * p0; r < 2 * (p0 + PG); ++r)
@@ -483,7 +513,7 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
           }
         }
       }
-    }
+    });
   } else {
     if (prev.on)
 #pragma unroll

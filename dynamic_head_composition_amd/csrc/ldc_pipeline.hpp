@@ -44,4 +44,11 @@ __device__ __forceinline__ NextStage next_stage(int phase, int j, int H, int Hp,
   return {np, nj};
 }
 
+// The next stage's DMA is issued in kIssueParts parts spread over the
+// current stage: a wave that issues its whole share right after the barrier
+// can wait thousands of cycles for the memory pipeline to take it while its
+// SIMD partner computes alone.  Part p covers instructions
+// [p*N/kIssueParts, (p+1)*N/kIssueParts) of a wave's N.
+constexpr int kIssueParts = 4;
+
 }  // namespace ldc
