@@ -39,7 +39,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   constexpr int NT = NW * kWave;
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
-  __shared__ int s_doc[R];
+  __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
@@ -77,39 +77,20 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   auto issue_rest = [&](int phase, int j, auto bc, auto from) {
     static_for<decltype(from)::value, kIssueParts>([&](auto pp) { issue_part(phase, j, bc, pp); });
   };
+  // Prologue: the first tile, the document ids, the saved shared map and the
+  // first head's register operands are all in flight before the one wait.
   issue(0, 0, true, Buf<0>{});
-
-  for (int r = threadIdx.x; r < R; r += NT) {
-    const int s = span0 + r;
-    s_doc[r] = (s >= 0 && s < a.T) ? a.doc[s] : 0;
-  }
-  __syncthreads();
-  uint32_t mbits = 0;
-  {
-    const int dt = s_doc[brow + kHalo + n];
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = brow + 16 * b + 4 * g + i;
-        const int s = span0 + r;
-        const bool ok = tval & (s >= 0) & (s <= t) & (t - s < a.window) & (s_doc[r] == dt);
-        mbits |= (ok ? 1u : 0u) << (4 * b + i);
-      }
-  }
-  const uint32_t full = full_blocks(mbits);  // wave-uniform
-
+  issue_doc<R, NW>(s_doc, a.doc, span0, a.T);
   const float sl2 = a.scale * kLog2e;
   const int qb = (q0 >> 4) + w;         // this wave's 16-query block
   const bool wval = q0 + 16 * w < a.T;  // the block holds at least one query
   const size_t bandw = (size_t)(wval ? qb : 0) * kBandWords + (4 * g) * 16 + n;
-
   // The shared map saved by the forward pass (masked entries are stored as 0).
-  f32x4 pb[kKeyBlocks];
+  uint32_t bandv[kKeyBlocks][4];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pb[b][i] = band_decode<T>(a.band[bandw + b * 256 + i * 16]);
+    for (int i = 0; i < 4; ++i) bandv[b][i] = a.band[bandw + b * 256 + i * 16];
 
   // Per-head register operands are loaded one stage ahead (slot j%2 holds head j).
   RowFrag<T, D> fb[2];
@@ -127,6 +108,28 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     sb[1 - B] = scal[(size_t)tc * H + hn];
     if (st) stb[1 - B] = a.stats[(size_t)tc * H + hn];
   };
+  preload(dO, a.g, false);
+  wait_dma();
+
+  uint32_t mbits = 0;
+  {
+    const int dt = s_doc[brow + kHalo + n];
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = brow + 16 * b + 4 * g + i;
+        const int s = span0 + r;
+        const bool ok = tval & (s >= 0) & (s <= t) & (t - s < a.window) & (s_doc[r] == dt);
+        mbits |= (ok ? 1u : 0u) << (4 * b + i);
+      }
+  }
+  const uint32_t full = full_blocks(mbits);  // wave-uniform
+  f32x4 pb[kKeyBlocks];
+#pragma unroll
+  for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[b][i] = band_decode<T>(bandv[b][i]);
 
   // ---- phase 0 (V_h staged): B_h = dO_h V_h^T, dPbar, dG ----
   // Small results are stored at the start of the next stage, after its
@@ -140,7 +143,6 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     if (dg_h >= 0 && tval && g == 0) a.dg[(size_t)t * H + dg_h] = dg_val;
     dg_h = -1;
   };
-  preload(dO, a.g, false);
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
     const T* cur = B == 0 ? s_x0 : s_x1;
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
   __shared__ __attribute__((aligned(16))) float s_sc0[NSC * RP];
   __shared__ __attribute__((aligned(16))) float s_sc1[NSC * RP];
-  __shared__ int s_doc[R];
+  __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
@@ -329,13 +331,24 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   auto issue_rest = [&](int phase, int j, auto bc, auto from) {
     static_for<decltype(from)::value, kIssueParts>([&](auto pp) { issue_part(phase, j, bc, pp); });
   };
+  // Prologue: the first tile, the document ids and the saved shared map are
+  // all in flight before the one wait.
   issue(0, 0, true, Buf<0>{});
+  issue_doc<R, NW>(s_doc, a.doc, span0, a.T);
+  // Pbar (phase 0) and dPbar (phase 1) of this lane's (key, 4 queries)
+  // entries, from the bands: query block kq + b, key block 7 - b, 16 bytes
+  // per block; entries beyond the stream or outside the window read as 0.
+  const int kq = (k0 >> 4) + w;
+  const int nqb = (a.T + 15) >> 4;
+  auto band_word = [&](int b) {
+    const int qbk = kq + b < nqb ? kq + b : nqb - 1;
+    return (size_t)qbk * kBandWords + (7 - b) * 256 + n * 16 + 4 * g;
+  };
+  uint4 bandv[kKeyBlocks];
+#pragma unroll
+  for (int b = 0; b < kKeyBlocks; ++b) bandv[b] = *reinterpret_cast<const uint4*>(a.band + band_word(b));
+  wait_dma();
 
-  for (int r = threadIdx.x; r < R; r += NT) {
-    const int t = span0 + r;
-    s_doc[r] = (t < a.T) ? a.doc[t] : 0;
-  }
-  __syncthreads();
   uint32_t mbits = 0;  // bit 4b+i <-> query row brow + 16b + 4g + i
   {
     const int ds = s_doc[brow + n];
@@ -350,21 +363,10 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
       }
   }
   const uint32_t full = full_blocks(mbits);  // wave-uniform
-
-  // Pbar (phase 0) and dPbar (phase 1) of this lane's (key, 4 queries)
-  // entries, from the bands: query block kq + b, key block 7 - b, 16 bytes
-  // per block; entries beyond the stream or outside the window read as 0.
-  const int kq = (k0 >> 4) + w;
-  const int nqb = (a.T + 15) >> 4;
-  auto band_word = [&](int b) {
-    const int qbk = kq + b < nqb ? kq + b : nqb - 1;
-    return (size_t)qbk * kBandWords + (7 - b) * 256 + n * 16 + 4 * g;
-  };
   f32x4 pb[kKeyBlocks];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) {
-    const uint4 u = *reinterpret_cast<const uint4*>(a.band + band_word(b));
-    const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+    const uint32_t uu[4] = {bandv[b].x, bandv[b].y, bandv[b].z, bandv[b].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) pb[b][i] = keep_admitted(mbits, b, i, band_decode<T>(uu[i]), 0.f);
   }

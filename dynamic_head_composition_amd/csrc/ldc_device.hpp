@@ -292,6 +292,15 @@ __device__ __forceinline__ void issue_scalars(float* arr, const float* __restric
   }
 }
 
+// Issue the DMA of the document ids of rows [row0, row0+R) into an LDS array
+// of round_up(R, 64) ints; rows outside [0,T) read as 0.
+template <int R, int NW>
+__device__ __forceinline__ void issue_doc(int* s_doc, const int32_t* __restrict__ doc, int row0,
+                                          int T_) {
+  issue_scalars<R, NW>(reinterpret_cast<float*>(s_doc), reinterpret_cast<const float*>(doc), 1, 0,
+                       row0, T_, 1, 0);
+}
+
 __device__ __forceinline__ void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

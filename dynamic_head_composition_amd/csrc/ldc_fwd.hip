@@ -31,7 +31,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   constexpr int NT = NW * kWave;
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
-  __shared__ int s_doc[R];
+  __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
@@ -60,13 +60,17 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     issue(ns.phase == 0 ? 0 : 1, ns.head >= 0 ? ns.head : 0, ns.head >= 0,
           Buf<1 - decltype(bc)::value>{});
   };
+  // Prologue: the first tile, the document ids and the first head's register
+  // operands are all in flight before the one wait.
   issue(0, 0, true, Buf<0>{});
-
-  for (int r = threadIdx.x; r < R; r += NT) {
-    const int s = span0 + r;
-    s_doc[r] = (s >= 0 && s < a.T) ? a.doc[s] : 0;
-  }
-  __syncthreads();
+  issue_doc<R, NW>(s_doc, a.doc, span0, a.T);
+  // Per-head register operands are loaded one stage ahead (slot j%2 holds
+  // head j), so their latency overlaps the previous stage's compute.
+  RowFrag<T, D> qfb[2];
+  float chb[2];  // rows t >= T are fully masked (coef 0), their loads use row T-1
+  load_row_frag<T, D>(qfb[0], q + (size_t)tc * H * D, g);
+  chb[0] = a.c[(size_t)tc * H];
+  wait_dma();
 
   // Admission mask of this lane's 32 band entries: bit 4b+i <-> key row brow+16b+4g+i.
   uint32_t mbits = 0;
@@ -88,13 +92,6 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   f32x4 pb[kKeyBlocks];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
-
-  // Per-head register operands are loaded one stage ahead (slot j%2 holds
-  // head j), so their latency overlaps the previous stage's compute.
-  RowFrag<T, D> qfb[2];
-  float chb[2];  // rows t >= T are fully masked (coef 0), their loads use row T-1
-  load_row_frag<T, D>(qfb[0], q + (size_t)tc * H * D, g);
-  chb[0] = a.c[(size_t)tc * H];
 
   // Softmax statistics of each head go to the saved state for the backward
   // pass; the store is deferred past the next stage's barrier.
