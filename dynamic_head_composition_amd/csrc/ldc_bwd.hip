@@ -151,6 +151,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     prefetch(j, bc, dO, a.g, false);
     flush_dg();
     issue_part(0, j, bc, Part<0>{});
+    __builtin_amdgcn_s_setprio(2);
     if (!real) {
       issue_rest(0, j, bc, Part<1>{});
       return;
@@ -174,6 +175,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
         dgs += pb[b][i] * bt[b][i];
         dpb[b][i] += gh * bt[b][i];
       }
+    __builtin_amdgcn_s_setprio(0);
     dg_val = wave_sum4(dgs);
     dg_h = j;
   });
@@ -214,6 +216,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     prefetch(j, bc, q, a.c, true);
     flush_dc();
     issue_part(1, j, bc, Part<0>{});
+    __builtin_amdgcn_s_setprio(2);
     if (!real) {
       issue_rest(1, j, bc, Part<1>{});
       flush_dq();
@@ -251,6 +254,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
       for (int i = 0; i < 4; ++i) p[b][i] = cs * p[b][i] * (dpb[b][i] - dcs);
     BandOperand<T> dso;
     dso.set(p);
+    __builtin_amdgcn_s_setprio(0);
     mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, prev);
     pend_h = j;
   });
@@ -397,6 +401,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     wait_dma();
     const bool real = j < H;
     issue_part(0, j, bc, Part<0>{});
+    __builtin_amdgcn_s_setprio(2);
     if (!real) {
       issue_rest(0, j, bc, Part<1>{});
       flush(a.dv, 1.f);
@@ -410,10 +415,12 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     }
     BandOperand<T> op;
     op.set(gp);
+    __builtin_amdgcn_s_setprio(1);
     mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n, pending(a.dv, 1.f), [&](auto pp) {
       if constexpr (decltype(pp)::value < kIssueParts) issue_part(0, j, bc, pp);
     });
     issue_rest(0, j, bc, Part<tcontract_groups<T, D>()>{});
+    __builtin_amdgcn_s_setprio(0);
     pend_h = j;
   });
 
@@ -439,6 +446,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     const PendingRow prev = pending(first ? a.dv : a.dk, first ? 1.f : a.scale);
     first = false;
     issue_part(1, j, bc, Part<0>{});
+    __builtin_amdgcn_s_setprio(2);
     if (!real) {
       issue_rest(1, j, bc, Part<1>{});
       if (prev.on) store_row_f32<T, D>(prev.row, pend, prev.scale, g);
@@ -468,6 +476,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     mask_band(p, mbits, full, 0.f);
     BandOperand<T> dso;
     dso.set(p);
+    __builtin_amdgcn_s_setprio(0);
     mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, prev);
     pend_h = j;
   });

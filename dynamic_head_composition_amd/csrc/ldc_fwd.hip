@@ -114,6 +114,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     chb[1 - B] = a.c[(size_t)tc * H + hn];
     __builtin_amdgcn_sched_barrier(0);
     issue_next(0, j, bc);
+    __builtin_amdgcn_s_setprio(2);
     if (!real) return;
     const RowFrag<T, D>& qf = qfb[B];
     const float ch = chb[B];
@@ -133,6 +134,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
+    __builtin_amdgcn_s_setprio(0);
     mx = wave_max4(mx);
     const float mxs = mx == -INFINITY ? 0.f : mx * sl2;  // a row with no key: all terms 0
     float sum = 0.f;
@@ -191,12 +193,14 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     ghb[1 - B] = a.g[(size_t)tc * H + (j + 1 < H ? j + 1 : 0)];
     __builtin_amdgcn_sched_barrier(0);
     issue_next(1, j, bc);
+    __builtin_amdgcn_s_setprio(2);
     if (!real) {
       flush();
       return;
     }
     const float gh = ghb[B];
     mma_tcontract<T, D>(pend, cur, brow, lo, pop, g, n, pending());
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int r = 0; r < D / 16; ++r) pend[r] *= gh;
     pend_h = j;
