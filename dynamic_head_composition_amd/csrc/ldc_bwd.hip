@@ -36,7 +36,6 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   constexpr int BQ = 16 * NW;
   constexpr int R = BQ + kHalo;
-  constexpr int NT = NW * kWave;
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
   __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
@@ -272,7 +271,6 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   constexpr int BK = 16 * NW;
   constexpr int R = BK + kHalo;  // query rows [k0, k0 + BK + 112)
   constexpr int RP = (R + 63) / 64 * 64;
-  constexpr int NT = NW * kWave;
   // per-row scalars of the staged head: C, G, dC, row max, 1/row sum
   enum { SC_C = 0, SC_G = 1, SC_DC = 2, SC_MX = 3, SC_INV = 4, NSC = 5 };
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];

@@ -28,7 +28,6 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   constexpr int BQ = 16 * NW;
   constexpr int R = BQ + kHalo;
-  constexpr int NT = NW * kWave;
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
   __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
