@@ -47,7 +47,10 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
 
   const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, n = lane & 15;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  // Tiles in reverse order: the first workgroups then work on the tiles the
+  // forward pass touched last, whose inputs are still in the memory-side
+  // cache; the key-side kernel runs forward and so starts where this one ends.
+  const int tile = gridDim.x - 1 - xcd_tile(blockIdx.x, gridDim.x);
   const int q0 = tile * BQ;
   const int span0 = q0 - kHalo;
   const int brow = 16 * w;
