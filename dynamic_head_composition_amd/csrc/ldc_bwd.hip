@@ -39,6 +39,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
   __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
+  __shared__ __attribute__((aligned(16))) float s_xp[Elem<T>::bf16 ? NW * 512 : 4];  // row stores
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
@@ -198,15 +199,15 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   // contraction (see mma_tcontract), late in the stage: stores issued early
   // would queue ahead of the other waves' DMA of the next tile.
   auto pending = [&]() {
-    return PendingRow{a.dq + ((size_t)t * H + (pend_h >= 0 ? pend_h : 0)) * D, a.scale, pend_h >= 0 && tval};
+    return pending_rows<D>(a.dq, q0 + 16 * w, n, a.T, H, pend_h >= 0 ? pend_h : 0, pend_h >= 0,
+                           a.scale, s_xp + (Elem<T>::bf16 ? w * 512 : 0));
   };
   auto flush_dc = [&]() {
     if (pend_h >= 0 && tval && g == 0) a.dc[(size_t)t * H + pend_h] = dc_val;
   };
   auto flush_dq = [&]() {
     flush_dc();
-    const PendingRow pr = pending();
-    if (pr.on) store_row_f32<T, D>(pr.row, pend, a.scale, g);
+    store_row<T, D>(pending(), pend, g, n);
     pend_h = -1;
   };
   preload(q, a.c, true);
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float s_sc0[NSC * RP];
   __shared__ __attribute__((aligned(16))) float s_sc1[NSC * RP];
   __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
+  __shared__ __attribute__((aligned(16))) float s_xp[Elem<T>::bf16 ? NW * 512 : 4];  // row stores
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
@@ -386,11 +388,11 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   f32x4 pend[D / 16];
   int pend_h = -1;
   auto pending = [&](float* dst, float scale) {
-    return PendingRow{dst + ((size_t)s * H + (pend_h >= 0 ? pend_h : 0)) * D, scale, pend_h >= 0 && sval};
+    return pending_rows<D>(dst, k0 + 16 * w, n, a.T, H, pend_h >= 0 ? pend_h : 0, pend_h >= 0, scale,
+                           s_xp + (Elem<T>::bf16 ? w * 512 : 0));
   };
   auto flush = [&](float* dst, float scale) {
-    const PendingRow pr = pending(dst, scale);
-    if (pr.on) store_row_f32<T, D>(pr.row, pend, scale, g);
+    store_row<T, D>(pending(dst, scale), pend, g, n);
     pend_h = -1;
   };
 
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     __builtin_amdgcn_s_setprio(2);
     if (!real) {
       issue_rest(1, j, bc, Part<1>{});
-      if (prev.on) store_row_f32<T, D>(prev.row, pend, prev.scale, g);
+      store_row<T, D>(prev, pend, g, n);
       pend_h = -1;
       return;
     }

@@ -31,6 +31,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
   __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
+  __shared__ __attribute__((aligned(16))) float s_xp[Elem<T>::bf16 ? NW * 512 : 4];  // row stores
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
@@ -177,11 +178,11 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   f32x4 pend[D / 16];
   int pend_h = -1;
   auto pending = [&]() {
-    return PendingRow{o + ((size_t)t * H + (pend_h >= 0 ? pend_h : 0)) * D, 1.f, pend_h >= 0 && tval};
+    return pending_rows<D>(o, q0 + 16 * w, n, a.T, H, pend_h >= 0 ? pend_h : 0, pend_h >= 0, 1.f,
+                           s_xp + (Elem<T>::bf16 ? w * 512 : 0));
   };
   auto flush = [&]() {
-    const PendingRow pr = pending();
-    if (pr.on) store_row_f32<T, D>(pr.row, pend, 1.f, g);
+    store_row<T, D>(pending(), pend, g, n);
     pend_h = -1;
   };
   for_stage_pairs(Hp, [&](int j, auto bc) {
