@@ -151,7 +151,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     const T* cur = B == 0 ? s_x0 : s_x1;
     wait_dma();
     const bool real = j < H;
-    prefetch(j, bc, dO, a.g, false);
+    // the last stage of this phase prefetches the first head of the next one
+    const bool last = j + 1 >= H;
+    prefetch(j, bc, last ? q : dO, last ? a.c : a.g, last);
     flush_dg();
     issue_part(0, j, bc, Part<0>{});
     __builtin_amdgcn_s_setprio(2);
@@ -210,7 +212,6 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     store_row<T, D>(pending(), pend, g, n);
     pend_h = -1;
   };
-  preload(q, a.c, true);
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
     const T* cur = B == 0 ? s_x0 : s_x1;
@@ -396,6 +397,19 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     pend_h = -1;
   };
 
+  // Q phase operands loaded during the last dO stage: dPbar of this lane's
+  // (key, 4 queries) entries and the first head's K fragment.
+  f32x4 dpb[kKeyBlocks];
+  RowFrag<T, D> kfb[2];
+  auto load_q_phase = [&]() {
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      const float4 d4 = *reinterpret_cast<const float4*>(a.dband + band_word(b));
+      dpb[b] = f32x4{d4.x, d4.y, d4.z, d4.w};  // only multiplied by P_h, which is 0 where masked
+    }
+    load_row_frag<T, D>(kfb[0], k + (size_t)sc_ * H * D, g);
+  };
+
   // ---- phase 0 (dO_h staged): dV_h = (G_h o Pbar)^T dO_h ----
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
@@ -404,6 +418,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     wait_dma();
     const bool real = j < H;
     issue_part(0, j, bc, Part<0>{});
+    if (j + 1 >= H) load_q_phase();
     __builtin_amdgcn_s_setprio(2);
     if (!real) {
       issue_rest(0, j, bc, Part<1>{});
@@ -428,14 +443,6 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   });
 
   // ---- phase 1 (Q_h staged): P_h, dS_h, dK_h = scale dS_h^T Q_h ----
-  f32x4 dpb[kKeyBlocks];
-#pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) {
-    const float4 d4 = *reinterpret_cast<const float4*>(a.dband + band_word(b));
-    dpb[b] = f32x4{d4.x, d4.y, d4.z, d4.w};  // only multiplied by P_h, which is 0 where masked
-  }
-  RowFrag<T, D> kfb[2];
-  load_row_frag<T, D>(kfb[0], k + (size_t)sc_ * H * D, g);
   bool first = true;
   for_stage_pairs(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
