@@ -87,13 +87,13 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   const float sl2 = a.scale * kLog2e;
   const int qb = (q0 >> 4) + w;         // this wave's 16-query block
   const bool wval = q0 + 16 * w < a.T;  // the block holds at least one query
-  const size_t bandw = (size_t)(wval ? qb : 0) * kBandWords + (4 * g) * 16 + n;
+  const size_t bandb = (size_t)(wval ? qb : 0) * kBandWords;  // this wave's band block
   // The shared map saved by the forward pass (masked entries are stored as 0).
   uint32_t bandv[kKeyBlocks][4];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bandv[b][i] = a.band[bandw + b * 256 + i * 16];
+    for (int i = 0; i < 4; ++i) bandv[b][i] = a.band[bandb + b * 256 + (4 * g + i) * 16 + n];
 
   // Per-head register operands are loaded one stage ahead (slot j%2 holds head j).
   RowFrag<T, D> fb[2];
@@ -187,10 +187,20 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   flush_dg();
   if (wval) {
     // dPbar of this wave's block, for the key-centric kernel
+    uint32_t* blk = reinterpret_cast<uint32_t*>(a.dband) + bandb;
+    if constexpr (Elem<T>::bf16) {
+      uint32_t wv[kKeyBlocks][4];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+      for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a.dband[bandw + b * 256 + i * 16] = dpb[b][i];
+        for (int i = 0; i < 4; ++i) wv[b][i] = __float_as_uint(dpb[b][i]);
+      store_band_block(blk, wv, s_xp + w * 512, g, n);
+    } else {
+#pragma unroll
+      for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) blk[b * 256 + (4 * g + i) * 16 + n] = __float_as_uint(dpb[b][i]);
+    }
   }
 
   // ---- phase 1 (K_h staged): P_h, dC, dS, dQ ----

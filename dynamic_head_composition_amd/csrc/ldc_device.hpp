@@ -625,6 +625,28 @@ __device__ __forceinline__ float band_decode(uint32_t u) {
     return __uint_as_float(u);
 }
 
+// A query-centric wave's band block (lane (g, n) holds words (4g+i)*16 + n
+// of key block b, i = 0..3) stored as whole 1 KB lines: through the wave's 2 KB LDS scratch, two key blocks at a time, so
+// each instruction covers one contiguous key block (lane l: words 4l..4l+3)
+// instead of 32 scattered 4-byte accesses per lane.  `blk` is the block's
+// first word (16-byte aligned); one wave's scratch accesses follow each other
+// in LDS order, so no barrier is needed.
+__device__ __forceinline__ void store_band_block(uint32_t* blk, const uint32_t (&wv)[kKeyBlocks][4],
+                                                 float* xp, int g, int n) {
+  uint32_t* xs = reinterpret_cast<uint32_t*>(xp);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < kKeyBlocks / 2; ++r) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[bb * 256 + (4 * g + i) * 16 + n] = wv[2 * r + bb][i];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+      *reinterpret_cast<uint4*>(blk + (2 * r + bb) * 256 + 4 * lane) =
+          *reinterpret_cast<const uint4*>(xs + bb * 256 + 4 * lane);
+  }
+}
 // Workgroup -> tile map that gives each XCD a contiguous run of tiles, so the
 // halo rows a tile shares with its neighbour are fetched through the same L2.
 // (Workgroups are dispatched to the 8 XCDs round-robin by block index.)

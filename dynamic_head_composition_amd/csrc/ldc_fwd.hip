@@ -163,11 +163,20 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   pop.set(pb);
   if (a.band && q0 + 16 * w < a.T) {
     // the wave's 16 x 128 shared map, for the backward pass
-    uint32_t* dst = a.band + (size_t)((q0 >> 4) + w) * kBandWords + (4 * g) * 16 + n;
+    uint32_t* blk = a.band + (size_t)((q0 >> 4) + w) * kBandWords;
+    if constexpr (Elem<T>::bf16) {
+      uint32_t wv[kKeyBlocks][4];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+      for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[b * 256 + i * 16] = band_encode<T>(pb[b][i]);
+        for (int i = 0; i < 4; ++i) wv[b][i] = band_encode<T>(pb[b][i]);
+      store_band_block(blk, wv, s_xp + w * 512, g, n);
+    } else {
+#pragma unroll
+      for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) blk[b * 256 + (4 * g + i) * 16 + n] = band_encode<T>(pb[b][i]);
+    }
   }
 
   // ---- phase 1 (V_h staged): O^T_h = V_h^T Pbar^T, scaled by G ----
