@@ -153,11 +153,11 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     const bool real = j < H;
     // the last stage of this phase prefetches the first head of the next one
     const bool last = j + 1 >= H;
-    prefetch(j, bc, last ? q : dO, last ? a.c : a.g, last);
     flush_dg();
     issue_part(0, j, bc, Part<0>{});
     __builtin_amdgcn_s_setprio(2);
     if (!real) {
+      prefetch(j, bc, last ? q : dO, last ? a.c : a.g, last);
       issue_rest(0, j, bc, Part<1>{});
       return;
     }
@@ -172,6 +172,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
       if (b == 3) issue_part(0, j, bc, Part<2>{});
       if (b == 5) issue_part(0, j, bc, Part<3>{});
     }
+    // next stage's register operands, issued after this stage's DMA and
+    // contraction (right after the barrier every wave's issue would contend)
+    prefetch(j, bc, last ? q : dO, last ? a.c : a.g, last);
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
@@ -227,7 +230,6 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     const T* cur = B == 0 ? s_x0 : s_x1;
     wait_dma();
     const bool real = j < H;
-    prefetch(j, bc, q, a.c, true);
     flush_dc();
     issue_part(1, j, bc, Part<0>{});
     __builtin_amdgcn_s_setprio(2);
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
       if (b == 3) issue_part(1, j, bc, Part<2>{});
       if (b == 5) issue_part(1, j, bc, Part<3>{});
     }
+    prefetch(j, bc, q, a.c, true);  // next stage's operands (see the V phase)
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
@@ -460,7 +463,6 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     const float* sc = B == 0 ? s_sc0 : s_sc1;
     wait_dma();
     const bool real = j < H;
-    load_row_frag<T, D>(kfb[1 - B], k + ((size_t)sc_ * H + (j + 1 < H ? j + 1 : 0)) * D, g);
     // the first stage of this phase stores the last dV row (during its token
     // contraction, late in the stage: see the query-side kernel)
     const PendingRow prev = pending(first ? a.dv : a.dk, first ? 1.f : a.scale);
@@ -482,6 +484,8 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
       if (b == 3) issue_part(1, j, bc, Part<2>{});
       if (b == 5) issue_part(1, j, bc, Part<3>{});
     }
+    // next head's K row, issued after this stage's DMA and score contraction
+    load_row_frag<T, D>(kfb[1 - B], k + ((size_t)sc_ * H + (j + 1 < H ? j + 1 : 0)) * D, g);
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
       const float4 mx = rows4(sc, SC_MX, b), inv = rows4(sc, SC_INV, b);
