@@ -46,6 +46,10 @@ SMALL = [  # (T, H, d, dtype, window, docs, seed)
     # a whole number of 128-token tiles; several tiles per XCD
     (256, 6, 128, "bf16", 112, ("single",), 22),
     (4096, 6, 128, "bf16", 112, ("geometric", 1024), 23),
+    # the last wave holds 9 and 8 rows: the whole-line row stores have one
+    # and zero active lanes in their second half
+    (265, 2, 128, "bf16", 112, ("geometric", 60), 24),
+    (136, 4, 64, "bf16", 64, ("uniform", 8, 40), 25),
 ]
 
 
