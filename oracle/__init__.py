@@ -7,6 +7,8 @@ and it imports nothing from the product path.
 Modules:
   ldc_oracle  blocked numpy float64 forward/backward (the oracle proper)
   bruteforce  dense torch float64 forward for pinning on tiny inputs
+  mudd_oracle float64 multiway dynamic dense (MUDD) layer mixing, forward
+              and backward
 
 Parity status: every function here is pinned by CPU tests (brute force,
 library special cases, closed forms, invariants, finite differences and a
