@@ -2,6 +2,7 @@
 """Throughput of the Lightweight DC layer (forward + backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py --workload mudd     # MUDD layer mixing (fwd + bwd) instead
 
 A step is one forward pass and one backward pass of the layer over the whole
 synthetic token stream of the workload (inputs resident in HBM before timing):
@@ -15,6 +16,10 @@ heads of dim 128, window 112, documents of geometric length with mean 1024)
 is seeded and synthetic; it stands in for the FineWeb token stream the
 speedrun trains on.  The CPU baseline times the fp64 oracle on the host cores
 over a bounded leading part of the same stream.
+
+With --workload mudd the step is one MUDD mix forward and backward
+(mudd_fwd + mudd_bwd) over a GPT-2 small token stream (65,536 tokens, model
+dim 768, 13 layer streams, 4 ways), reported in the same format.
 """
 from __future__ import annotations
 
@@ -36,6 +41,9 @@ MFMA_F32_PEAK_TFLOPS = 157.3
 METRIC = "LDC attention fwd+bwd tokens/s on 1 MI355X (GPT-2-small shape); % MFMA peak"
 KERNELS = ("ldc_fwd", "ldc_bwd_q", "ldc_bwd_kv")
 SOURCES = ("ldc_device.hpp", "ldc_pipeline.hpp", "ldc_fwd.hip", "ldc_bwd.hip", "ldc_internal.h")
+MUDD_METRIC = "MUDD layer mixing fwd+bwd tokens/s on 1 MI355X (GPT-2-small stream)"
+MUDD_KERNELS = ("mudd_fwd", "mudd_bwd")
+MUDD_SOURCES = ("mudd.hip", "mudd_internal.h")
 
 
 def log(*a):
@@ -73,15 +81,15 @@ def algorithmic_bytes_per_token(H: int, d: int, elem: int) -> dict:
     }
 
 
-def source_digest() -> str:
+def source_digest(files=SOURCES) -> str:
     h = hashlib.sha256()
-    for f in SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "dynamic_head_composition_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, files=SOURCES):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when it is missing or was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -91,7 +99,7 @@ def measured_traffic(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     ent = rec.get(workload, {}).get(kernel)
-    if not ent or ent.get("source_digest") != source_digest():
+    if not ent or ent.get("source_digest") != source_digest(files):
         return None
     return ent.get("bytes_per_launch")
 
@@ -118,6 +126,124 @@ def cpu_baseline(w, budget_s: float, chunk: int = 8192):
                       f"in {chunk}-token slices with their window halo; {el:.1f} s"}
 
 
+def mudd_bytes_per_token(dm: int, W: int, J: int, elem: int) -> dict:
+    """Compulsory HBM bytes per token of the two MUDD kernels."""
+    return {
+        # J streams and the W x J weights in; W float32 mixes out
+        "mudd_fwd": J * dm * elem + W * J * 4 + W * dm * 4,
+        # J streams, W upstream gradients and the weights in; J float32 stream
+        # gradients and the W x J weight gradients out
+        "mudd_bwd": (J + W) * dm * elem + W * J * 4 + J * dm * 4 + W * J * 4,
+    }
+
+
+def mudd_cpu_baseline(w, budget_s: float, chunk: int = 2048):
+    """Time the fp64 MUDD oracle (forward + backward) on leading row slices
+    until `budget_s` seconds of CPU work or the whole stream."""
+    from oracle import mudd_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.T and time.perf_counter() - t0 < budget_s:
+        lo, hi = done, min(w.T, done + chunk)
+        xs = [x[lo:hi] for x in w.xs]
+        mo.forward(xs, w.a[lo:hi])
+        mo.backward(xs, w.a[lo:hi], [d[lo:hi] for d in w.dys])
+        done = hi
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward over tokens [0, {done}) of the same stream, "
+                      f"in {chunk}-token slices; {el:.1f} s"}
+
+
+def bench_mudd(args):
+    import torch
+    import dynamic_head_composition_amd as ldc
+    from dynamic_head_composition_amd import mudd
+    from dynamic_head_composition_amd import workloads as wl
+
+    ldc.load_library()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    cfg = dict(wl.MUDD_BENCH)
+    if args.tokens:
+        cfg["T"] = args.tokens
+    log(f"generating MUDD workload {cfg} ...")
+    w = wl.make_mudd_workload(**cfg)
+    xs, a, dys = w.torch_inputs("cuda")
+    T, dm, W, J = w.T, w.dm, w.W, w.J
+    elem = 2 if w.dtype == "bf16" else 4
+    f32 = dict(dtype=torch.float32, device="cuda")
+    ys = [torch.empty((T, dm), **f32) for _ in range(W)]
+    dxs = [torch.empty((T, dm), **f32) for _ in range(J)]
+    da = torch.empty((T, W, J), **f32)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        mudd.fwd(xs, a, out=ys)
+        if evs:
+            evs[1].record()
+        mudd.bwd(xs, a, dys, out=(dxs, da))
+        if evs:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if not all(bool(torch.isfinite(t).all()) for t in ys + dxs + [da]):
+        raise SystemExit("non-finite outputs")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = {kn: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                 for j, kn in enumerate(MUDD_KERNELS)}
+    bpt = mudd_bytes_per_token(dm, W, J, elem)
+    per_kernel = {kn: {"avg_us": round(kernel_ms[kn] * 1e3, 2), "alg_bytes_per_launch": bpt[kn] * T,
+                       "alg_GBps": round(bpt[kn] * T / (kernel_ms[kn] * 1e-3) / 1e9, 1)}
+                  for kn in MUDD_KERNELS}
+    dominant = max(MUDD_KERNELS, key=lambda kn: kernel_ms[kn])
+    achieved = bpt[dominant] * T / (kernel_ms[dominant] * 1e-3) / 1e9
+    value = T / (ms_per_step * 1e-3)
+    ceiling_tps = HBM_PEAK_GBPS * 1e9 / sum(bpt.values())
+    line = {
+        "metric": MUDD_METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "model_dim": dm, "ways": W, "streams": J,
+                   "recipe": w.recipe, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(dominant, w.name, MUDD_SOURCES)},
+        "step_hbm_ceiling_tokens_per_s": round(ceiling_tps, 1),
+        "step_roofline_frac": round(value / ceiling_tps, 4),
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = mudd_cpu_baseline(w, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +252,8 @@ def main():
     # (measured: 5 warm-up steps read ~10% below 100); 100 steps take ~50 ms
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = GPT-2 small layer fwd+bwd)")
+    ap.add_argument("--workload", choices=("ldc", "mudd"), default="ldc",
+                    help="ldc: the Lightweight DC layer (default); mudd: MUDD layer mixing")
     ap.add_argument("--tokens", type=int, default=None, help="truncate the stream (quick runs only)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -139,6 +267,8 @@ def main():
         print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "mudd":
+        return bench_mudd(args)
 
     import torch
     import dynamic_head_composition_amd as ldc

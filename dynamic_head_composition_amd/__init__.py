@@ -63,6 +63,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ldc_status_str.restype = ctypes.c_char_p
     lib.ldc_version.argtypes = []
     lib.ldc_version.restype = i32
+    lib.mudd_fwd.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp, vp]
+    lib.mudd_fwd.restype = i32
+    lib.mudd_bwd.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.mudd_bwd.restype = i32
     _lib = lib
     return lib
 

@@ -1,4 +1,4 @@
-"""Build the HIP library libldc.so in-tree for gfx950.
+"""Build the HIP library libldc.so (Lightweight DC and MUDD mixing) in-tree for gfx950.
 
     python -m dynamic_head_composition_amd.build [--verbose]
 
@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libldc.so")
-SOURCES = ["ldc_fwd.hip", "ldc_bwd.hip", "ldc_api.cpp"]
+SOURCES = ["ldc_fwd.hip", "ldc_bwd.hip", "ldc_api.cpp", "mudd.hip", "mudd_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -251,3 +251,65 @@ def config_workload(i: int, T: Optional[int] = None) -> Workload:
         cfg["name"] = cfg["name"] + f"_trunc{T}"
     return make_workload(**cfg)
 
+
+
+# ----------------------------------------------------------------------------
+# MUDD layer mixing (AITNT page, section "第一刀—砍层间")
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class MuddWorkload:
+    """Inputs of a MUDD mix: J layer streams X_j [T, dm], weights A [T, W, J]
+    and the upstream gradients dY_w [T, dm] of the W ways."""
+    name: str
+    T: int
+    dm: int
+    W: int
+    J: int
+    dtype: str          # storage type of the streams and of dY
+    xs: list            # J arrays [T, dm] float32 (representable in `dtype`)
+    a: np.ndarray       # [T, W, J] float32
+    dys: list           # W arrays [T, dm] float32 (representable in `dtype`)
+    recipe: str = ""
+
+    def slice(self, lo: int, hi: int) -> "MuddWorkload":
+        return dataclasses.replace(self, name=f"{self.name}[{lo}:{hi}]", T=hi - lo,
+                                   xs=[x[lo:hi] for x in self.xs], a=self.a[lo:hi],
+                                   dys=[d[lo:hi] for d in self.dys])
+
+    def torch_inputs(self, device="cuda"):
+        """(xs, a, dys) as torch tensors on `device`, streams in the storage dtype."""
+        import torch
+
+        def big(x):
+            if self.dtype == "bf16":
+                return torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(device)
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+        return ([big(x) for x in self.xs],
+                torch.from_numpy(np.ascontiguousarray(self.a)).to(device),
+                [big(d) for d in self.dys])
+
+
+def make_mudd_workload(T: int, dm: int, W: int, J: int, *, dtype: str = "bf16", seed: int = 0,
+                       a_std: float = 0.5, name: Optional[str] = None) -> MuddWorkload:
+    """Seeded MUDD inputs.  Draw order (one PCG64 stream): X_0 .. X_{J-1}
+    ~ N(0, 1), A ~ N(0, a_std^2) (weights of both signs, as the page allows),
+    dY_0 .. dY_{W-1} ~ N(0, 1); streams and dY rounded to bf16 (RNE) for
+    bf16 workloads."""
+    if dtype not in ("bf16", "f32"):
+        raise ValueError("dtype must be 'bf16' or 'f32'")
+    rng = np.random.default_rng(seed)
+    rnd = round_bf16 if dtype == "bf16" else (lambda x: x)
+    xs = [rnd(_normal(rng, (T, dm))) for _ in range(J)]
+    a = (_normal(rng, (T, W, J)) * np.float32(a_std)).astype(np.float32)
+    dys = [rnd(_normal(rng, (T, dm))) for _ in range(W)]
+    nm = name or f"mudd_T{T}_dm{dm}_W{W}_J{J}_{dtype}"
+    recipe = (f"T={T} tokens, dm={dm}, {W} way(s), {J} streams, {dtype}; X, dY ~ N(0,1), "
+              f"A ~ N(0,{a_std}^2), seed {seed}")
+    return MuddWorkload(nm, T, dm, W, J, dtype, xs, a, dys, recipe)
+
+
+# The mixing workload the benchmark times: a GPT-2 small stream (65,536 tokens,
+# model_dim 768) at the widest point of a 12-layer model (embedding plus 12
+# layer outputs) with the four ways of full MUDD.
+MUDD_BENCH = dict(T=65536, dm=768, W=4, J=13, dtype="bf16", seed=11)

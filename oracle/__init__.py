@@ -1,4 +1,4 @@
-"""CPU oracle of the Lightweight DC layer (fp64).
+"""CPU oracles (fp64): the Lightweight DC layer and MUDD layer mixing.
 
 TEST INFRASTRUCTURE: imported only by tests, the smoke check and the CPU
 baseline of the benchmark.  The product path never imports, calls or links it,
