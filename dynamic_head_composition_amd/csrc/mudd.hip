@@ -16,7 +16,9 @@
 // contiguous bytes of a float32 row.  Loads are unconditional (lanes past the
 // row end read column 0 of the row and are masked afterwards) so a batch of
 // them is in flight before the first use.  Rows are processed in groups of SG
-// slots (SG x 256 columns) to bound registers.
+// slots (SG x 256 columns) to bound registers.  Every load and store is
+// non-temporal: no element is touched twice, and keeping the streams out of
+// the caches measured 4-10% faster than ordinary accesses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,14 +31,19 @@ constexpr int kWaves = 4;  // waves per workgroup
 
 typedef uint16_t bf16_t;
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // Four consecutive stored elements, kept in their storage form until used so
 // that a batch of loads is in flight before any conversion.
 template <typename T>
 struct Raw;
 template <>
 struct Raw<bf16_t> {
-  uint2 u;
-  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+  u32x2 u;
+  __device__ __forceinline__ void load(const bf16_t* p) {
+    u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  }
   __device__ __forceinline__ float4 f() const {
     return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                   __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
@@ -44,10 +51,16 @@ struct Raw<bf16_t> {
 };
 template <>
 struct Raw<float> {
-  float4 v;
-  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
-  __device__ __forceinline__ float4 f() const { return v; }
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  }
+  __device__ __forceinline__ float4 f() const { return float4{v.x, v.y, v.z, v.w}; }
 };
+
+__device__ __forceinline__ void store_nt(float* p, const float4& v) {
+  __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+}
 
 __device__ __forceinline__ void fma4(float4& acc, float s, const float4& x) {
   acc.x = fmaf(s, x.x, acc.x);
@@ -121,7 +134,7 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_kernel(const FwdArgs a) {
 #pragma unroll
         for (int s = 0; s < SG; ++s) {
           const int col = 256 * (s0 + s) + 4 * lane;
-          if (col < dm) *reinterpret_cast<float4*>(yw + col) = acc[w][s];
+          if (col < dm) store_nt(yw + col, acc[w][s]);
         }
       }
     }
@@ -131,30 +144,33 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_kernel(const FwdArgs a) {
 // ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------
-// Sum of v[i] over the 64 lanes for all 64 indices at once: each step halves
-// the values a lane holds, keeping the half selected by one lane bit and
-// adding the partner lane's copy of it, so after six steps lane l holds the
-// total of index l (63 shuffles instead of 6 per index).
-template <int N>
-__device__ __forceinline__ void reduce_step(float (&v)[64], int lane) {
+// One halving step of a sum over lanes of N values at once: lanes that differ
+// in bit M pair up; each keeps the half of the values selected by that bit
+// and adds its partner's copy of that half.
+template <int N, int M>
+__device__ __forceinline__ void reduce_step(float (&v)[16], int lane) {
   constexpr int H = N / 2;
-  const bool up = (lane & H) != 0;
+  const bool up = (lane & M) != 0;
 #pragma unroll
   for (int i = 0; i < H; ++i) {
     const float send = up ? v[i] : v[i + H];
     const float keep = up ? v[i + H] : v[i];
-    v[i] = keep + __shfl_xor(send, H);
+    v[i] = keep + __shfl_xor(send, M);
   }
 }
 
-__device__ __forceinline__ float transpose_reduce64(float (&v)[64], int lane) {
-  reduce_step<64>(v, lane);
-  reduce_step<32>(v, lane);
-  reduce_step<16>(v, lane);
-  reduce_step<8>(v, lane);
-  reduce_step<4>(v, lane);
-  reduce_step<2>(v, lane);
-  return v[0];
+// Sum of v[i] over the 64 lanes for all 16 indices: four halving steps on
+// lane bits 5..2 (index bits 3..0) and two plain steps on bits 1..0, so lane
+// l ends with the total of index (l >> 2) & 15 (17 shuffles instead of 96).
+__device__ __forceinline__ float transpose_reduce16(float (&v)[16], int lane) {
+  reduce_step<16, 32>(v, lane);
+  reduce_step<8, 16>(v, lane);
+  reduce_step<4, 8>(v, lane);
+  reduce_step<2, 4>(v, lane);
+  float x = v[0];
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 1);
+  return x;
 }
 
 template <typename T, int SG>
@@ -167,10 +183,11 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_kernel(const BwdArgs a) {
   for (int64_t t = (int64_t)blockIdx.x * kWaves + wv; t < a.T; t += stride) {
     const float wl = lane < W * J ? a.a[t * (W * J) + lane] : 0.f;
     const size_t row = (size_t)t * dm;
-    // partial dA of this lane, index w * 16 + j
-    float p[64];
+    // dA of the streams of batch b (4b .. 4b+3), summed over the wave: lane l
+    // holds (w, j) = ((l >> 4) & 3, 4b + ((l >> 2) & 3))
+    float red[kMaxJ / 4];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) p[i] = 0.f;
+    for (int b = 0; b < kMaxJ / 4; ++b) red[b] = 0.f;
     for (int s0 = 0; s0 < nslot; s0 += SG) {
       int colc[SG];  // this lane's columns, clamped into the row
 #pragma unroll
@@ -208,6 +225,9 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_kernel(const BwdArgs a) {
 #pragma unroll
           for (int s = 0; s < SG; ++s) xv[jj][s].load(xj + colc[s]);
         }
+        float p[16];  // this lane's part of dA, index w * 4 + jj
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int j = j0 + jj;
@@ -222,16 +242,20 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_kernel(const BwdArgs a) {
             for (int w = 0; w < kMaxW; ++w) {
               if (w >= W) break;
               fma4(d, weight(wl, w * J + j), dyv[w][s]);
-              p[w * 16 + j] = dot4(dyv[w][s], x, p[w * 16 + j]);
+              p[w * 4 + jj] = dot4(dyv[w][s], x, p[w * 4 + jj]);
             }
-            if (col < dm) *reinterpret_cast<float4*>(dxj + col) = d;
+            if (col < dm) store_nt(dxj + col, d);
           }
         }
+        red[j0 / 4] += transpose_reduce16(p, lane);
       }
     }
-    const float tot = transpose_reduce64(p, lane);
-    const int w = lane >> 4, j = lane & 15;
-    if (w < W && j < J) a.da[t * (W * J) + w * J + j] = tot;
+    const int w = (lane >> 4) & 3, jj = (lane >> 2) & 3;
+#pragma unroll
+    for (int b = 0; b < kMaxJ / 4; ++b) {
+      const int j = 4 * b + jj;
+      if ((lane & 3) == 0 && w < W && j < J) a.da[t * (W * J) + w * J + j] = red[b];
+    }
   }
 }
 
