@@ -126,6 +126,18 @@ def cpu_baseline(w, budget_s: float, chunk: int = 8192):
                       f"in {chunk}-token slices with their window halo; {el:.1f} s"}
 
 
+def copy_probe(mib: int) -> None:
+    """One plain device copy of `mib` MiB: a kernel of known traffic against
+    which rocprofv3's HBM byte counters are calibrated."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def mudd_bytes_per_token(dm: int, W: int, J: int, elem: int) -> dict:
     """Compulsory HBM bytes per token of the two MUDD kernels."""
     return {
@@ -192,6 +204,8 @@ def bench_mudd(args):
         if evs:
             evs[2].record()
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -306,12 +320,7 @@ def main():
             evs[3].record()
 
     if args.copy_probe_mib:
-        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(args.copy_probe_mib)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
