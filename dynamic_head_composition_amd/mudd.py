@@ -5,6 +5,7 @@ kernels; if the library is missing the calls raise.
 
     ys = fwd(xs, a)              # W float32 tensors [T, dm]
     dxs, da = bwd(xs, a, dys)    # J float32 tensors [T, dm], float32 [T, W, J]
+    ys = mudd_mix(xs, a)         # autograd-aware: W tensors in the dtype of xs
 
 xs: J tensors [T, dm] (bfloat16 or float32, one dtype), a: float32 [T, W, J],
 dys: W tensors [T, dm] in the dtype of xs.  The mix is the one the AITNT page
@@ -17,7 +18,7 @@ import ctypes
 
 from . import LDCError, _dtype_code, load_library
 
-__all__ = ["fwd", "bwd", "MAX_STREAMS", "MAX_WAYS", "MAX_DIM"]
+__all__ = ["fwd", "bwd", "mudd_mix", "MuddFunction", "MAX_STREAMS", "MAX_WAYS", "MAX_DIM"]
 
 MAX_STREAMS, MAX_WAYS, MAX_DIM = 16, 4, 16384
 
@@ -85,3 +86,44 @@ def bwd(xs, a, dys, out=None, stream=None):
     if st != 0:
         raise LDCError(st, "mudd_bwd")
     return dxs, da
+
+
+def _make_function():
+    import torch
+
+    class MuddFunction(torch.autograd.Function):
+        """Autograd wrapper: forward = mudd_fwd, backward = mudd_bwd.  Outputs
+        and stream gradients are cast back to the dtype of the streams."""
+
+        @staticmethod
+        def forward(ctx, a, *xs):
+            ys = fwd(list(xs), a)
+            ctx.save_for_backward(a, *xs)
+            return tuple(y.to(xs[0].dtype) for y in ys)
+
+        @staticmethod
+        def backward(ctx, *dys):
+            a, *xs = ctx.saved_tensors
+            dys = [(torch.zeros_like(xs[0]) if d is None else d.contiguous().to(xs[0].dtype)) for d in dys]
+            dxs, da = bwd(xs, a, dys)
+            return (da,) + tuple(d.to(xs[0].dtype) for d in dxs)
+
+    return MuddFunction
+
+
+_fn = None
+
+
+def __getattr__(name):
+    global _fn
+    if name == "MuddFunction":
+        if _fn is None:
+            _fn = _make_function()
+        return _fn
+    raise AttributeError(name)
+
+
+def mudd_mix(xs, a):
+    """The W mixes of the streams `xs` with weights `a` [T, W, J], through
+    autograd (gradients flow to every stream and to the weights)."""
+    return list(__getattr__("MuddFunction").apply(a, *xs))

@@ -120,3 +120,24 @@ def test_binding_rejects_bad_shapes(ldc):
         mudd.fwd([x], torch.zeros((4, 1, 2), device="cuda"))
     with pytest.raises(ValueError):
         mudd.bwd([x], torch.zeros((4, 2, 1), device="cuda"), [x])
+
+
+def test_autograd_matches_oracle(ldc):
+    """mudd_mix through torch autograd: gradients of sum_w <dY_w, Y_w> with
+    respect to the streams and the weights equal the oracle's backward."""
+    import torch
+    from dynamic_head_composition_amd import mudd
+    w = wl.make_mudd_workload(77, 256, 2, 3, dtype="f32", seed=14)
+    xs, a, dys = w.torch_inputs("cuda")
+    xs = [x.requires_grad_() for x in xs]
+    a.requires_grad_()
+    ys = mudd.mudd_mix(xs, a)
+    loss = sum((y * d).sum() for y, d in zip(ys, dys))
+    loss.backward()
+    rdx, rda = mo.backward(w.xs, w.a, w.dys)
+    ry = mo.forward(w.xs, w.a)
+    for k in range(w.W):
+        check(f"y{k}", ys[k].detach().cpu().numpy(), ry[k])
+    for j in range(w.J):
+        check(f"dx{j}", xs[j].grad.cpu().numpy(), rdx[j])
+    check("da", a.grad.cpu().numpy(), rda)
