@@ -16,11 +16,20 @@ from __future__ import annotations
 
 import ctypes
 
-from . import LDCError, _dtype_code, load_library
+from . import LDC_BF16, LDC_F32, LDCError, load_library
 
 __all__ = ["fwd", "bwd", "mudd_mix", "MuddFunction", "MAX_STREAMS", "MAX_WAYS", "MAX_DIM"]
 
 MAX_STREAMS, MAX_WAYS, MAX_DIM = 16, 4, 16384
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LDC_BF16
+    if t.dtype == torch.float32:
+        return LDC_F32
+    raise TypeError(f"streams must be bfloat16 or float32, got {t.dtype}")
 
 
 def _ptrs(ts):
