@@ -1,8 +1,8 @@
 """Plain fp64 CPU oracle of multiway dynamic dense (MUDD) layer mixing.
 
 TEST INFRASTRUCTURE.  Only tests, the smoke check and the CPU-baseline leg of
-the benchmark may import this module.  It shares no code with the HIP path and imports nothing
-from it.
+the benchmark may import this module.  It shares no code with the HIP path and
+imports nothing from it.
 
 What is computed (AITNT page "一个国产AI小透明，连续两次刷新NanoGPT Speedrun
 世界纪录", section "第一刀—砍层间", and the MUDD remarks in section "和业界其他
