@@ -50,6 +50,11 @@ SMALL = [  # (T, H, d, dtype, window, docs, seed)
     # and zero active lanes in their second half
     (265, 2, 128, "bf16", 112, ("geometric", 60), 24),
     (136, 4, 64, "bf16", 64, ("uniform", 8, 40), 25),
+    # one head on the bf16 paths (a single real stage and a padding stage per
+    # phase), and sixteen heads of 64 (GPT-2 medium's attention shape)
+    (150, 1, 128, "bf16", 112, ("geometric", 50), 26),
+    (97, 1, 64, "bf16", 20, ("uniform", 8, 30), 27),
+    (300, 16, 64, "bf16", 112, ("geometric", 80), 28),
 ]
 
 
