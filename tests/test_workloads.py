@@ -62,3 +62,23 @@ def test_config_recipes():
     neg = w4.c <= -4.0
     assert 0.07 < neg.mean() < 0.13
     assert np.all((w4.g >= 0) & (w4.g <= 2))
+
+
+def test_mudd_workload_seeded_shapes_and_dtypes():
+    a = wl.make_mudd_workload(40, 96, 3, 5, seed=3)
+    b = wl.make_mudd_workload(40, 96, 3, 5, seed=3)
+    assert len(a.xs) == 5 and len(a.dys) == 3 and a.a.shape == (40, 3, 5)
+    for u, v in zip(a.xs + a.dys + [a.a], b.xs + b.dys + [b.a]):
+        assert u.dtype == np.float32 and np.array_equal(u, v)
+    for x in a.xs + a.dys:
+        assert x.shape == (40, 96) and np.array_equal(wl.round_bf16(x), x)
+    assert (a.a < 0).any() and (a.a > 0).any()  # weights of both signs
+    c = wl.make_mudd_workload(40, 96, 3, 5, seed=4)
+    assert not np.array_equal(a.xs[0], c.xs[0])
+    s = a.slice(10, 20)
+    assert s.T == 10 and np.array_equal(s.xs[2], a.xs[2][10:20]) and np.array_equal(s.a, a.a[10:20])
+
+
+def test_mudd_workload_f32_not_rounded():
+    w = wl.make_mudd_workload(16, 8, 1, 2, dtype="f32", seed=1)
+    assert not all(np.array_equal(wl.round_bf16(x), x) for x in w.xs)
