@@ -313,17 +313,21 @@ __device__ __forceinline__ void wait_dma() {
 // over the head dimension (global memory source; the caller passes a valid
 // row and ignores the result of lanes it does not need).
 // bf16: chunk kk holds d = 32kk + 8g .. +7.  fp32: slot kk holds d = g*D/4 + kk.
-template <typename T, int D>
+// NT: non-temporal loads (the caller reads each such row once).
+template <typename T, int D, bool NT = false>
 __device__ __forceinline__ void load_row_frag(RowFrag<T, D>& f, const T* __restrict__ row, int g) {
   if constexpr (Elem<T>::bf16) {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      f.v[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + 32 * kk + 8 * g));
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(row + 32 * kk + 8 * g);
+      f.v[kk] = __builtin_bit_cast(bf16x8, NT ? __builtin_nontemporal_load(src) : *src);
+    }
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 4; kk += 4) {
-      const float4 u = *reinterpret_cast<const float4*>(row + g * (D / 4) + kk);
-      f.v[kk] = u.x; f.v[kk + 1] = u.y; f.v[kk + 2] = u.z; f.v[kk + 3] = u.w;
+      const f32x4* src = reinterpret_cast<const f32x4*>(row + g * (D / 4) + kk);
+      const f32x4 u = NT ? __builtin_nontemporal_load(src) : *src;
+      f.v[kk] = u[0]; f.v[kk + 1] = u[1]; f.v[kk + 2] = u[2]; f.v[kk + 3] = u[3];
     }
   }
 }
@@ -432,8 +436,14 @@ __device__ __forceinline__ int tcontract_d(int r, int g) {
     return 16 * r + 4 * g;
 }
 
+// Output rows are written once and never read back by the kernel that writes
+// them, so every output store is non-temporal (streaming): it does not take
+// cache lines from the input tiles whose halo rows neighbouring workgroups
+// share through L2.  Measured at the GPT-2 small layer: forward -13%,
+// backward kernels -4 to -7%.
 __device__ __forceinline__ void store4(float* dst, f32x4 v, float s) {
-  *reinterpret_cast<float4*>(dst) = float4{v[0] * s, v[1] * s, v[2] * s, v[3] * s};
+  __builtin_nontemporal_store(f32x4{v[0] * s, v[1] * s, v[2] * s, v[3] * s},
+                              reinterpret_cast<f32x4*>(dst));
 }
 
 // A wave's finished output rows (one per lane column n) still held in
@@ -643,8 +653,8 @@ __device__ __forceinline__ void store_band_block(uint32_t* blk, const uint32_t (
       for (int i = 0; i < 4; ++i) xs[bb * 256 + (4 * g + i) * 16 + n] = wv[2 * r + bb][i];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
-      *reinterpret_cast<uint4*>(blk + (2 * r + bb) * 256 + 4 * lane) =
-          *reinterpret_cast<const uint4*>(xs + bb * 256 + 4 * lane);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(xs + bb * 256 + 4 * lane),
+                                  reinterpret_cast<u32x4*>(blk + (2 * r + bb) * 256 + 4 * lane));
   }
 }
 // Workgroup -> tile map that gives each XCD a contiguous run of tiles, so the

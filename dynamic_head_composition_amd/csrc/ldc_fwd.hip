@@ -65,10 +65,13 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
   issue(0, 0, true, Buf<0>{});
   issue_doc<R, NW>(s_doc, a.doc, span0, a.T);
   // Per-head register operands are loaded one stage ahead (slot j%2 holds
-  // head j), so their latency overlaps the previous stage's compute.
+  // head j), so their latency overlaps the previous stage's compute.  Each Q
+  // row is read once here, so its loads are non-temporal (measured 1% faster
+  // over the forward and backward together; the backward kernels' register
+  // operands measured slower that way and load normally).
   RowFrag<T, D> qfb[2];
   float chb[2];  // rows t >= T are fully masked (coef 0), their loads use row T-1
-  load_row_frag<T, D>(qfb[0], q + (size_t)tc * H * D, g);
+  load_row_frag<T, D, true>(qfb[0], q + (size_t)tc * H * D, g);
   chb[0] = a.c[(size_t)tc * H];
   wait_dma();
 
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(const FwdArgs a) {
     wait_dma();
     const bool real = j < H;
     const int hn = j + 1 < H ? j + 1 : 0;
-    load_row_frag<T, D>(qfb[1 - B], q + ((size_t)tc * H + hn) * D, g);
+    load_row_frag<T, D, true>(qfb[1 - B], q + ((size_t)tc * H + hn) * D, g);
     chb[1 - B] = a.c[(size_t)tc * H + hn];
     __builtin_amdgcn_sched_barrier(0);
     issue_next(0, j, bc);
