@@ -89,11 +89,13 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   const bool wval = q0 + 16 * w < a.T;  // the block holds at least one query
   const size_t bandb = (size_t)(wval ? qb : 0) * kBandWords;  // this wave's band block
   // The shared map saved by the forward pass (masked entries are stored as 0).
+  // Each band word is read once here: non-temporal loads (bwd_q -1%).
   uint32_t bandv[kKeyBlocks][4];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bandv[b][i] = a.band[bandb + b * 256 + (4 * g + i) * 16 + n];
+    for (int i = 0; i < 4; ++i)
+      bandv[b][i] = __builtin_nontemporal_load(a.band + bandb + b * 256 + (4 * g + i) * 16 + n);
 
   // Per-head register operands are loaded one stage ahead (slot j%2 holds head j).
   RowFrag<T, D> fb[2];
@@ -359,6 +361,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   // Pbar (phase 0) and dPbar (phase 1) of this lane's (key, 4 queries)
   // entries, from the bands: query block kq + b, key block 7 - b, 16 bytes
   // per block; entries beyond the stream or outside the window read as 0.
+  // Loaded non-temporally, like every band read (bwd_kv -3%).
   const int kq = (k0 >> 4) + w;
   const int nqb = (a.T + 15) >> 4;
   auto band_word = [&](int b) {
@@ -367,7 +370,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   };
   uint4 bandv[kKeyBlocks];
 #pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) bandv[b] = *reinterpret_cast<const uint4*>(a.band + band_word(b));
+  for (int b = 0; b < kKeyBlocks; ++b)
+    bandv[b] = __builtin_bit_cast(
+        uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.band + band_word(b))));
   wait_dma();
 
   uint32_t mbits = 0;  // bit 4b+i <-> query row brow + 16b + 4g + i
@@ -417,8 +422,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   auto load_q_phase = [&]() {
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) {
-      const float4 d4 = *reinterpret_cast<const float4*>(a.dband + band_word(b));
-      dpb[b] = f32x4{d4.x, d4.y, d4.z, d4.w};  // only multiplied by P_h, which is 0 where masked
+      const f32x4 d4 =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.dband + band_word(b)));
+      dpb[b] = d4;  // only multiplied by P_h, which is 0 where masked
     }
     load_row_frag<T, D>(kfb[0], k + (size_t)sc_ * H * D, g);
   };
