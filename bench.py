@@ -7,7 +7,15 @@
 A step is one forward pass and one backward pass of the layer over the whole
 synthetic token stream of the workload (inputs resident in HBM before timing):
 ldc_fwd, then ldc_bwd as its two kernels ldc_bwd_q and ldc_bwd_kv, each timed
-with HIP events on the stream it runs on.  Rank 0 prints one JSON line.
+with HIP events on the stream it runs on (median and interquartile range over
+the timed steps).  Rank 0 prints one JSON line.
+
+The roofline figures use the algorithmic bytes of each pass: the compulsory
+I/O of the layer's definition, every input read once and every output written
+once (forward 6,196 B/token, backward 15,460 B/token at 6 x 128 bf16).  The
+bytes the kernels move as designed (float32 O, the saved state, the backward
+workspace, the key-side kernel's second read of Q, K and dO) and the measured
+HBM traffic (rocprofv3 counters) are reported beside them.
 The default warm-up (100 untimed steps, ~50 ms) brings the GPU from idle to
 its sustained clocks before the timed steps.
 
@@ -40,6 +48,8 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 MFMA_F32_PEAK_TFLOPS = 157.3
 METRIC = "LDC attention fwd+bwd tokens/s on 1 MI355X (GPT-2-small shape); % MFMA peak"
 KERNELS = ("ldc_fwd", "ldc_bwd_q", "ldc_bwd_kv")
+# the launches of each pass of the layer (a pass is one ABI call)
+PASSES = {"ldc_fwd": ("ldc_fwd",), "ldc_bwd": ("ldc_bwd_q", "ldc_bwd_kv")}
 SOURCES = ("ldc_device.hpp", "ldc_pipeline.hpp", "ldc_fwd.hip", "ldc_bwd.hip", "ldc_internal.h")
 MUDD_METRIC = "MUDD layer mixing fwd+bwd tokens/s on 1 MI355X (GPT-2-small stream)"
 MUDD_KERNELS = ("mudd_fwd", "mudd_bwd")
@@ -61,12 +71,23 @@ def valid_pairs(doc: np.ndarray, window: int) -> int:
     return int(np.minimum(idx - first + 1, window).sum())
 
 
-def algorithmic_bytes_per_token(H: int, d: int, elem: int) -> dict:
-    """Compulsory HBM bytes per token of each kernel: every input it must read
-    and every output it must write, once.  The saved state of the forward is
-    512 B/token of shared-map band (2,048 four-byte words per 16 tokens) plus
-    8 B per (token, head) of softmax statistics; the backward workspace holds
-    the dPbar band (512 B/token)."""
+def spec_bytes_per_token(H: int, d: int, elem: int) -> dict:
+    """Algorithmic HBM bytes per token of each pass: the compulsory I/O of the
+    layer's definition, every tensor once, O counted in the storage dtype.
+    Forward: Q, K, V, C, G, doc in; O out.  Backward: Q, K, V, dO, C, G, doc
+    in; dQ, dK, dV (float32), dC, dG out.  At 6 x 128 bf16: 6,196 and 15,460."""
+    row = H * d
+    return {"ldc_fwd": 3 * row * elem + 8 * H + 4 + row * elem,
+            "ldc_bwd": 4 * row * elem + 16 * H + 4 + 3 * row * 4}
+
+
+def design_bytes_per_token(H: int, d: int, elem: int) -> dict:
+    """HBM bytes per token each kernel moves as designed: its inputs read once
+    and its outputs written once, including the state the kernels pass each
+    other (the shared-map band, 512 B/token, and the softmax statistics, 8 B
+    per token and head, saved by the forward; the dPbar band, 512 B/token, in
+    the backward workspace) and the key-side kernel's second read of Q, K and
+    dO.  O and the gradients are float32."""
     row = H * d
     ch = 4 * H    # one float per (token, head)
     band = 512    # shared-map or dPbar band
@@ -89,41 +110,81 @@ def source_digest(files=SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str, files=SOURCES):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when it is missing or was taken on other kernel sources."""
+def measured_traffic(kernels, workload: str, files=SOURCES):
+    """HBM bytes per launch summed over `kernels` (the launches of one pass),
+    from the committed rocprofv3 counter summary, or None when an entry is
+    missing or was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get(workload, {}).get(kernel)
-    if not ent or ent.get("source_digest") != source_digest(files):
-        return None
-    return ent.get("bytes_per_launch")
+    total = 0
+    for kernel in kernels:
+        ent = rec.get(workload, {}).get(kernel)
+        if not ent or ent.get("source_digest") != source_digest(files):
+            return None
+        total += ent["bytes_per_launch"]
+    return total
 
 
-def cpu_baseline(w, budget_s: float, chunk: int = 8192):
-    """Time the fp64 oracle (forward + backward) on leading slices of the
-    stream until `budget_s` seconds of CPU work or the whole stream."""
-    from oracle import ldc_oracle as orc
+def host_cpu() -> dict:
+    """CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cores": len(os.sched_getaffinity(0))}
+
+
+def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    done = 0
-    t0 = time.perf_counter()
-    while done < w.T and time.perf_counter() - t0 < budget_s:
-        lo, hi = done, min(w.T, done + chunk)
-        orc.forward_slice(w.q, w.k, w.v, w.c, w.g, w.doc, lo, hi, window=w.window, scale=w.scale)
-        orc.backward_slice(w.q, w.k, w.v, w.c, w.g, w.doc, w.do, lo, hi, window=w.window, scale=w.scale)
-        done = hi
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle forward+backward over tokens [0, {done}) of the same stream, "
-                      f"in {chunk}-token slices with their window halo; {el:.1f} s"}
+        return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def stats_us(samples_ms) -> dict:
+    """Median and interquartile range (µs) of per-step event times."""
+    a = np.asarray(samples_ms, dtype=np.float64) * 1e3
+    q1, med, q3 = np.percentile(a, [25, 50, 75])
+    return {"median_us": round(float(med), 2), "iqr_us": round(float(q3 - q1), 2),
+            "mean_us": round(float(a.mean()), 2)}
+
+
+def cpu_baseline(w, budget_s: float, chunk: int = 8192, runs: int = 3):
+    """Time the fp64 oracle (forward + backward) on leading slices of the
+    stream: up to `runs` passes over the whole stream (the median is
+    reported), or one pass over a leading part when a pass would exceed
+    `budget_s` seconds."""
+    from oracle import ldc_oracle as orc
+    rates = []
+    t_all = time.perf_counter()
+    for _ in range(runs):
+        done = 0
+        t0 = time.perf_counter()
+        while done < w.T and time.perf_counter() - t0 < budget_s:
+            lo, hi = done, min(w.T, done + chunk)
+            orc.forward_slice(w.q, w.k, w.v, w.c, w.g, w.doc, lo, hi, window=w.window, scale=w.scale)
+            orc.backward_slice(w.q, w.k, w.v, w.c, w.g, w.doc, w.do, lo, hi, window=w.window,
+                               scale=w.scale)
+            done = hi
+        rates.append(done / (time.perf_counter() - t0))
+        if done < w.T or time.perf_counter() - t_all > budget_s:
+            break
+    el = time.perf_counter() - t_all
+    return {"value": float(np.median(rates)), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle", **host_cpu(),
+            "sample": f"fp64 numpy oracle forward+backward over tokens [0, {done}) of the same stream "
+                      f"in {chunk}-token slices with their window halo; median of {len(rates)} "
+                      f"pass(es), {el:.1f} s in all"}
 
 
 def copy_probe(mib: int) -> None:
@@ -153,11 +214,6 @@ def mudd_cpu_baseline(w, budget_s: float, chunk: int = 2048):
     """Time the fp64 MUDD oracle (forward + backward) on leading row slices
     until `budget_s` seconds of CPU work or the whole stream."""
     from oracle import mudd_oracle as mo
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     done = 0
     t0 = time.perf_counter()
     while done < w.T and time.perf_counter() - t0 < budget_s:
@@ -167,7 +223,8 @@ def mudd_cpu_baseline(w, budget_s: float, chunk: int = 2048):
         mo.backward(xs, w.a[lo:hi], [d[lo:hi] for d in w.dys])
         done = hi
     el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": done / el, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            **host_cpu(),
             "sample": f"fp64 oracle forward+backward over tokens [0, {done}) of the same stream, "
                       f"in {chunk}-token slices; {el:.1f} s"}
 
@@ -218,14 +275,15 @@ def bench_mudd(args):
     if not all(bool(torch.isfinite(t).all()) for t in ys + dxs + [da]):
         raise SystemExit("non-finite outputs")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kernel_ms = {kn: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
-                 for j, kn in enumerate(MUDD_KERNELS)}
+    kstat = {kn: stats_us([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])
+             for j, kn in enumerate(MUDD_KERNELS)}
     bpt = mudd_bytes_per_token(dm, W, J, elem)
-    per_kernel = {kn: {"avg_us": round(kernel_ms[kn] * 1e3, 2), "alg_bytes_per_launch": bpt[kn] * T,
-                       "alg_GBps": round(bpt[kn] * T / (kernel_ms[kn] * 1e-3) / 1e9, 1)}
+    per_kernel = {kn: {**kstat[kn], "alg_bytes_per_launch": bpt[kn] * T,
+                       "alg_GBps": round(bpt[kn] * T / (kstat[kn]["median_us"] * 1e-6) / 1e9, 1)}
                   for kn in MUDD_KERNELS}
-    dominant = max(MUDD_KERNELS, key=lambda kn: kernel_ms[kn])
-    achieved = bpt[dominant] * T / (kernel_ms[dominant] * 1e-3) / 1e9
+    dominant = max(MUDD_KERNELS, key=lambda kn: kstat[kn]["median_us"])
+    achieved = bpt[dominant] * T / (kstat[dominant]["median_us"] * 1e-6) / 1e9
+    traffic = measured_traffic([dominant], w.name, MUDD_SOURCES)
     value = T / (ms_per_step * 1e-3)
     ceiling_tps = HBM_PEAK_GBPS * 1e9 / sum(bpt.values())
     line = {
@@ -245,7 +303,8 @@ def bench_mudd(args):
                    "recipe": w.recipe, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(dominant, w.name, MUDD_SOURCES)},
+                     "traffic": traffic,
+                     "traffic_over_alg": None if traffic is None else round(traffic / (bpt[dominant] * T), 3)},
         "step_hbm_ceiling_tokens_per_s": round(ceiling_tps, 1),
         "step_roofline_frac": round(value / ceiling_tps, 4),
         "kernels": per_kernel,
@@ -335,26 +394,32 @@ def main():
         raise SystemExit("non-finite outputs")
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kernel_ms = {kname: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
-                 for j, kname in enumerate(KERNELS)}
+    span = lambda a, b: [evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)]
+    # events: 0 before ldc_fwd, 1 after it, 2 after ldc_bwd_q, 3 after ldc_bwd_kv
+    kstat = {kn: stats_us(span(j, j + 1)) for j, kn in enumerate(KERNELS)}
+    pstat = {"ldc_fwd": stats_us(span(0, 1)), "ldc_bwd": stats_us(span(1, 3))}
     pairs = valid_pairs(w.doc, w.window)
     total_flops = 14.0 * H * d * pairs
-    bpt = algorithmic_bytes_per_token(H, d, elem)
-    per_kernel = {}
-    for kname in KERNELS:
-        sec = kernel_ms[kname] * 1e-3
-        per_kernel[kname] = {"avg_us": round(kernel_ms[kname] * 1e3, 2),
-                             "alg_bytes_per_launch": bpt[kname] * T,
-                             "alg_GBps": round(bpt[kname] * T / sec / 1e9, 1)}
-    dominant = max(KERNELS, key=lambda kname: kernel_ms[kname])
-    dom_sec = kernel_ms[dominant] * 1e-3
-    achieved = bpt[dominant] * T / dom_sec / 1e9
-    traffic = measured_traffic(dominant, w.name)
+    spec = spec_bytes_per_token(H, d, elem)
+    design = design_bytes_per_token(H, d, elem)
+    passes = {}
+    for pn, kernels in PASSES.items():
+        sec = pstat[pn]["median_us"] * 1e-6
+        alg = spec[pn] * T
+        traffic = measured_traffic(kernels, w.name)
+        passes[pn] = {**pstat[pn], "kernels": list(kernels), "alg_bytes_per_launch": alg,
+                      "alg_GBps": round(alg / sec / 1e9, 1),
+                      "frac": round(alg / sec / 1e9 / HBM_PEAK_GBPS, 4),
+                      "design_bytes_per_launch": sum(design[kn] for kn in kernels) * T,
+                      "traffic": traffic,
+                      "traffic_over_alg": None if traffic is None else round(traffic / alg, 3)}
+    per_kernel = {kn: {**kstat[kn], "design_bytes_per_launch": design[kn] * T} for kn in KERNELS}
+    dominant = max(PASSES, key=lambda pn: pstat[pn]["median_us"])
+    dom = passes[dominant]
     value = T / (ms_per_step * 1e-3)
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     alg_tflops = total_flops / (ms_per_step * 1e-3) / 1e12
-    alg_bytes_step = sum(bpt[kn] for kn in KERNELS) * T
-    ceiling_tps = HBM_PEAK_GBPS * 1e9 / (alg_bytes_step / T)
+    ceiling_tps = HBM_PEAK_GBPS * 1e9 / sum(spec.values())
 
     line = {
         "metric": METRIC,
@@ -371,13 +436,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "heads": H, "head_dim": d, "window": w.window,
                    "recipe": w.recipe, "valid_pairs": pairs, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic},
+        "roofline": {"bound": "hbm", "kernel": dominant, "launches": dom["kernels"],
+                     "achieved": dom["alg_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dom["frac"], "traffic": dom["traffic"],
+                     "traffic_over_alg": dom["traffic_over_alg"],
+                     "alg_bytes_per_launch": dom["alg_bytes_per_launch"],
+                     "design_bytes_per_launch": dom["design_bytes_per_launch"]},
         "mfma_peak_frac": round(alg_tflops / mfma_peak, 5),
         "alg_TFLOPs": round(alg_tflops, 2),
         "step_hbm_ceiling_tokens_per_s": round(ceiling_tps, 1),
         "step_roofline_frac": round(value / ceiling_tps, 4),
+        "passes": passes,
         "kernels": per_kernel,
     }
     if not args.no_cpu_baseline:

@@ -128,13 +128,6 @@ def _check(q, k, v, c, g, doc, do=None):
     return T, H, d
 
 
-def _stream(q, stream):
-    torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    return ctypes.c_void_p(stream.cuda_stream)
-
-
 def _buf(t):
     return (0, 0) if t is None else (t.data_ptr(), t.numel() * t.element_size())
 
@@ -143,22 +136,25 @@ def fwd(q, k, v, c, g, doc_ids, window: int = DEFAULT_WINDOW, scale: Optional[fl
         out=None, save: bool = False, saved=None, stream=None):
     """O[t,h,:] of the layer, float32 [T,H,d].  With save=True (or a `saved`
     buffer) also the state ldc_bwd needs, returned as (O, saved).  Enqueued on
-    `stream` (default: torch's current stream), not synchronised."""
+    `stream` (default: torch's current stream), not synchronised; tensors this
+    call allocates are allocated on that stream."""
     torch = _torch()
     lib = load_library()
     T, H, d = _check(q, k, v, c, g, doc_ids)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty(q.shape, dtype=torch.float32, device=q.device) if out is None else out
+    st_obj = torch.cuda.current_stream(q.device) if stream is None else stream
+    with torch.cuda.stream(st_obj):
+        o = torch.empty(q.shape, dtype=torch.float32, device=q.device) if out is None else out
+        if save and saved is None:
+            saved = torch.empty(max(16, saved_bytes(_dtype_code(q), T, H, d, window)),
+                                dtype=torch.uint8, device=q.device)
     if o.shape != q.shape or o.dtype != torch.float32 or not o.is_contiguous():
         raise ValueError("out must be a contiguous float32 tensor shaped like q")
-    if save and saved is None:
-        saved = torch.empty(max(16, saved_bytes(_dtype_code(q), T, H, d, window)), dtype=torch.uint8,
-                            device=q.device)
     sp, sn = _buf(saved)
     st = lib.ldc_fwd(_dtype_code(q), T, H, d, window, float(scale),
                      q.data_ptr(), k.data_ptr(), v.data_ptr(), c.data_ptr(), g.data_ptr(),
-                     doc_ids.data_ptr(), o.data_ptr(), sp, sn, _stream(q, stream))
+                     doc_ids.data_ptr(), o.data_ptr(), sp, sn, ctypes.c_void_p(st_obj.cuda_stream))
     if st != 0:
         raise LDCError(st, "ldc_fwd")
     return (o, saved) if saved is not None else o
@@ -168,20 +164,30 @@ def bwd(q, k, v, c, g, doc_ids, saved, do, window: int = DEFAULT_WINDOW,
         scale: Optional[float] = None, out=None, workspace=None, stream=None, part: str = "all"):
     """(dQ, dK, dV, dC, dG), all float32, given `saved` from fwd(..., save=True)
     on the same inputs.  part="q" or "kv" runs one of the two backward kernels
-    only (ldc_bwd_q / ldc_bwd_kv); "all" runs both."""
+    only (ldc_bwd_q / ldc_bwd_kv); "all" runs both.  part="kv" needs the
+    `workspace` a part="q" call filled for the same inputs (it reads dPbar
+    from there).  Tensors this call allocates are allocated on `stream`, so the
+    caching allocator does not hand them out while the kernels still use them."""
     torch = _torch()
     lib = load_library()
     T, H, d = _check(q, k, v, c, g, doc_ids, do)
+    if part not in ("all", "q", "kv"):
+        raise ValueError("part must be 'all', 'q' or 'kv'")
+    if part == "kv" and workspace is None:
+        raise ValueError("part='kv' reads the dPbar band a part='q' call wrote: pass that workspace")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        f32 = dict(dtype=torch.float32, device=q.device)
-        out = (torch.empty((T, H, d), **f32), torch.empty((T, H, d), **f32),
-               torch.empty((T, H, d), **f32), torch.empty((T, H), **f32), torch.empty((T, H), **f32))
+    st_obj = torch.cuda.current_stream(q.device) if stream is None else stream
+    with torch.cuda.stream(st_obj):
+        if out is None:
+            f32 = dict(dtype=torch.float32, device=q.device)
+            out = (torch.empty((T, H, d), **f32), torch.empty((T, H, d), **f32),
+                   torch.empty((T, H, d), **f32), torch.empty((T, H), **f32),
+                   torch.empty((T, H), **f32))
+        if workspace is None:
+            need = workspace_bytes(_dtype_code(q), T, H, d, window)
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     dq, dk, dv, dc, dg = out
-    need = workspace_bytes(_dtype_code(q), T, H, d, window)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     sp, sn = _buf(saved)
     wp, wn = _buf(workspace)
     entry = {"all": lib.ldc_bwd, "q": lib.ldc_bwd_q, "kv": lib.ldc_bwd_kv}[part]
@@ -189,7 +195,7 @@ def bwd(q, k, v, c, g, doc_ids, saved, do, window: int = DEFAULT_WINDOW,
                q.data_ptr(), k.data_ptr(), v.data_ptr(), c.data_ptr(), g.data_ptr(),
                doc_ids.data_ptr(), sp, sn, do.data_ptr(),
                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dc.data_ptr(), dg.data_ptr(),
-               wp, wn, _stream(q, stream))
+               wp, wn, ctypes.c_void_p(st_obj.cuda_stream))
     if st != 0:
         raise LDCError(st, {"all": "ldc_bwd", "q": "ldc_bwd_q", "kv": "ldc_bwd_kv"}[part])
     return dq, dk, dv, dc, dg
@@ -199,15 +205,20 @@ def _make_function():
     torch = _torch()
 
     class LDCFunction(torch.autograd.Function):
-        """Autograd wrapper: forward = ldc_fwd, backward = ldc_bwd (gradients
-        are cast back to the input dtypes)."""
+        """Autograd wrapper: forward = ldc_fwd, backward = ldc_bwd.
+
+        O is returned in float32 whatever the input dtype: a bf16 store alone
+        would round outputs of magnitude above ~5 by more than the bf16
+        tolerance (2e-2).  The incoming gradient is cast to the input dtype
+        for the kernels; the gradients of bf16 inputs are then rounded to bf16
+        by autograd, which gives a leaf the gradient dtype of the leaf."""
 
         @staticmethod
         def forward(ctx, q, k, v, c, g, doc_ids, window=DEFAULT_WINDOW, scale=None):
             o, saved = fwd(q, k, v, c, g, doc_ids, window, scale, save=True)
             ctx.save_for_backward(q, k, v, c, g, doc_ids, saved)
             ctx.window, ctx.scale = window, scale
-            return o.to(q.dtype)
+            return o
 
         @staticmethod
         def backward(ctx, do):

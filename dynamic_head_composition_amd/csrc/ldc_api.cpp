@@ -56,9 +56,15 @@ size_t ldc_saved_bytes(int dtype, int64_t T, int H, int d, int window) {
   return ldc::saved_band_bytes(T) + (size_t)T * (size_t)H * sizeof(float2);
 }
 
+// The backward pass's own scratch (the dPbar band), after room for the saved
+// state it recomputes when the caller passes none (256-byte aligned).
+static size_t bwd_own_bytes(int64_t T) { return ldc::saved_band_bytes(T); }
+static size_t state_room(size_t saved) { return (saved + 255) & ~(size_t)255; }
+
 size_t ldc_bwd_workspace_bytes(int dtype, int64_t T, int H, int d, int window) {
   if (check_common(dtype, T, H, d, window) != LDC_OK) return 0;
-  return ldc::saved_band_bytes(T);
+  if (T == 0) return 0;
+  return state_room(ldc_saved_bytes(dtype, T, H, d, window)) + bwd_own_bytes(T);
 }
 
 int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale, const void* q,
@@ -81,7 +87,7 @@ int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale, const v
   float2* stats = saved ? reinterpret_cast<float2*>(static_cast<char*>(saved) + ldc::saved_band_bytes(T))
                         : nullptr;
   ldc::FwdArgs a{(int)T, H, window, scale, q, k, v, c, g, doc_ids, o, band, stats};
-  hipError_t e = ldc::fwd_dispatch(dtype, d, a, static_cast<hipStream_t>(stream));
+  hipError_t e = ldc::fwd_dispatch(dtype, d, a, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
 
@@ -99,17 +105,37 @@ static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, 
     if (!p) return LDC_ERR_NULL;
   for (const void* p : ptrs)
     if (!aligned16(p)) return LDC_ERR_ALIGN;
-  if (!saved || saved_bytes < ldc_saved_bytes(dtype, T, H, d, window)) return LDC_ERR_WORKSPACE;
-  if (!aligned16(saved)) return LDC_ERR_ALIGN;
-  if (!workspace || workspace_bytes < ldc_bwd_workspace_bytes(dtype, T, H, d, window))
-    return LDC_ERR_WORKSPACE;
+  const size_t need_saved = ldc_saved_bytes(dtype, T, H, d, window);
+  if (saved) {
+    if (saved_bytes < need_saved) return LDC_ERR_WORKSPACE;
+    if (!aligned16(saved)) return LDC_ERR_ALIGN;
+  }
+  // Without saved state the workspace first holds the recomputed state.
+  const size_t need_ws = (saved ? 0 : state_room(need_saved)) + bwd_own_bytes(T);
+  if (!workspace || workspace_bytes < need_ws) return LDC_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LDC_ERR_ALIGN;
-  const uint32_t* band = static_cast<const uint32_t*>(saved);
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const void* state = saved;
+  if (!saved) {
+    state = ws;
+    ws += state_room(need_saved);
+    // The query-side kernel is the first reader of the state: recompute it
+    // there (the forward's score phase, band and statistics only).
+    if (parts & 1) {
+      ldc::FwdArgs f{(int)T, H, window, scale, q, k, v, c, g, doc_ids, nullptr,
+                     static_cast<uint32_t*>(const_cast<void*>(state)),
+                     reinterpret_cast<float2*>(static_cast<char*>(const_cast<void*>(state)) +
+                                               ldc::saved_band_bytes(T))};
+      if (ldc::fwd_dispatch(dtype, d, f, false, hs) != hipSuccess) return LDC_ERR_HIP;
+    }
+  }
+  const uint32_t* band = static_cast<const uint32_t*>(state);
   const float2* stats =
-      reinterpret_cast<const float2*>(static_cast<const char*>(saved) + ldc::saved_band_bytes(T));
+      reinterpret_cast<const float2*>(static_cast<const char*>(state) + ldc::saved_band_bytes(T));
   ldc::BwdArgs a{(int)T, H, window, scale, q, k, v, dO, c, g, doc_ids,
-                 dq, dk, dv, dc, dg, band, stats, static_cast<float*>(workspace)};
-  hipError_t e = ldc::bwd_dispatch(dtype, d, a, parts, static_cast<hipStream_t>(stream));
+                 dq, dk, dv, dc, dg, band, stats, reinterpret_cast<float*>(ws)};
+  hipError_t e = ldc::bwd_dispatch(dtype, d, a, parts, hs);
   return e == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
 

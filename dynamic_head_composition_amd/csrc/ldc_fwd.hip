@@ -17,7 +17,9 @@
 // column and 32 of its band entries: the softmax row reductions are in-lane
 // plus two cross-lane steps, and the composed map Pbar^T stays in registers
 // where it is directly the B operand of O^T = V^T Pbar^T (V^T read with LDS
-// transpose loads).  Pbar never leaves registers.
+// transpose loads).  When the caller asks for the saved state, each wave also
+// writes its 16 x 128 block of Pbar and each head's softmax statistics for the
+// backward pass.
 #include "ldc_device.hpp"
 #include "ldc_internal.h"
 #include "ldc_pipeline.hpp"
@@ -27,7 +29,10 @@ namespace ldc {
 // At d = 64 (bf16) a workgroup's LDS (77 KB) leaves room for a second one per
 // CU; asking for four waves per SIMD keeps the kernel within 128 VGPRs without
 // spills, and two workgroups per CU measured 4% faster there.
-template <typename T, int D, int NW>
+// VAL = false: the score phase only, writing the saved state (shared-map band
+// and softmax statistics) and no O: the backward pass's recomputation when the
+// caller kept no saved state.
+template <typename T, int D, int NW, bool VAL = true>
 __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) void fwd_kernel(
     const FwdArgs a) {
   constexpr int BQ = 16 * NW;
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
     issue_tile<T, D, R, NW>(buf, phase == 0 ? k : v, span0, a.T, H, h, on);
   };
   auto issue_next = [&](int phase, int j, auto bc) {
-    const NextStage ns = next_stage(phase, j, H, Hp, 2);
+    const NextStage ns = next_stage(phase, j, H, Hp, VAL ? 2 : 1);
     issue(ns.phase == 0 ? 0 : 1, ns.head >= 0 ? ns.head : 0, ns.head >= 0,
           Buf<1 - decltype(bc)::value>{});
   };
@@ -186,6 +191,11 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
     }
   }
 
+  if constexpr (!VAL) {
+    wait_dma();  // no DMA may land in LDS after the workgroup ends
+    return;
+  }
+
   // ---- phase 1 (V_h staged): O^T_h = V_h^T Pbar^T, scaled by G ----
   // A stage's output row is stored during the next stage, spread over its
   // contraction, after that stage's DMA has been issued.
@@ -226,21 +236,24 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
 }
 
 template <typename T, int D, int NW>
-static hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
+static hipError_t launch_fwd(const FwdArgs& a, bool value, hipStream_t st) {
   constexpr int BQ = 16 * NW;
   const int nblk = (int)((a.T + BQ - 1) / BQ);
-  hipLaunchKernelGGL((fwd_kernel<T, D, NW>), dim3(nblk), dim3(NW * kWave), 0, st, a);
+  if (value)
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, true>), dim3(nblk), dim3(NW * kWave), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, false>), dim3(nblk), dim3(NW * kWave), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, hipStream_t st) {
+hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, bool value, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 128) return launch_fwd<bf16_t, 128, 8>(a, st);
-    if (d == 64) return launch_fwd<bf16_t, 64, 8>(a, st);
+    if (d == 128) return launch_fwd<bf16_t, 128, 8>(a, value, st);
+    if (d == 64) return launch_fwd<bf16_t, 64, 8>(a, value, st);
   } else {
-    if (d == 128) return launch_fwd<float, 128, 2>(a, st);
-    if (d == 64) return launch_fwd<float, 64, 4>(a, st);
-    if (d == 16) return launch_fwd<float, 16, 4>(a, st);
+    if (d == 128) return launch_fwd<float, 128, 2>(a, value, st);
+    if (d == 64) return launch_fwd<float, 64, 4>(a, value, st);
+    if (d == 16) return launch_fwd<float, 16, 4>(a, value, st);
   }
   return hipErrorInvalidValue;
 }

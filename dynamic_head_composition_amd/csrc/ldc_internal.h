@@ -35,7 +35,8 @@ struct BwdArgs {
 inline size_t band_blocks(int64_t T) { return (size_t)((T + 15) / 16); }
 inline size_t saved_band_bytes(int64_t T) { return band_blocks(T) * kBandWordsHost * 4; }
 
-hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, hipStream_t st);
+// value = false: only the saved state (band and statistics), no O.
+hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, bool value, hipStream_t st);
 // parts: bit 0 = query-side kernel, bit 1 = key-side kernel
 hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, int parts, hipStream_t st);
 

@@ -61,10 +61,9 @@ def _check(xs, a, dys=None):
 
 
 def _stream(dev, stream):
+    """The stream to run on (torch's current one by default)."""
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    return ctypes.c_void_p(stream.cuda_stream)
+    return torch.cuda.current_stream(dev) if stream is None else stream
 
 
 def fwd(xs, a, out=None, stream=None):
@@ -72,10 +71,12 @@ def fwd(xs, a, out=None, stream=None):
     import torch
     lib = load_library()
     T, dm, W, J = _check(xs, a)
-    ys = out if out is not None else [torch.empty((T, dm), dtype=torch.float32, device=a.device)
-                                      for _ in range(W)]
+    s = _stream(a.device, stream)
+    with torch.cuda.stream(s):  # allocated on the stream that uses them
+        ys = out if out is not None else [torch.empty((T, dm), dtype=torch.float32, device=a.device)
+                                          for _ in range(W)]
     st = lib.mudd_fwd(_dtype_code(xs[0]), T, dm, W, J, _ptrs(xs), a.data_ptr(), _ptrs(ys),
-                      _stream(a.device, stream))
+                      ctypes.c_void_p(s.cuda_stream))
     if st != 0:
         raise LDCError(st, "mudd_fwd")
     return ys
@@ -86,12 +87,14 @@ def bwd(xs, a, dys, out=None, stream=None):
     import torch
     lib = load_library()
     T, dm, W, J = _check(xs, a, dys)
-    if out is None:
-        out = ([torch.empty((T, dm), dtype=torch.float32, device=a.device) for _ in range(J)],
-               torch.empty((T, W, J), dtype=torch.float32, device=a.device))
+    s = _stream(a.device, stream)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = ([torch.empty((T, dm), dtype=torch.float32, device=a.device) for _ in range(J)],
+                   torch.empty((T, W, J), dtype=torch.float32, device=a.device))
     dxs, da = out
     st = lib.mudd_bwd(_dtype_code(xs[0]), T, dm, W, J, _ptrs(xs), a.data_ptr(), _ptrs(dys),
-                      _ptrs(dxs), da.data_ptr(), _stream(a.device, stream))
+                      _ptrs(dxs), da.data_ptr(), ctypes.c_void_p(s.cuda_stream))
     if st != 0:
         raise LDCError(st, "mudd_bwd")
     return dxs, da
@@ -101,14 +104,15 @@ def _make_function():
     import torch
 
     class MuddFunction(torch.autograd.Function):
-        """Autograd wrapper: forward = mudd_fwd, backward = mudd_bwd.  Outputs
-        and stream gradients are cast back to the dtype of the streams."""
+        """Autograd wrapper: forward = mudd_fwd, backward = mudd_bwd.  The
+        mixes stay float32 (rounding them to bf16 would add the storage error
+        to every output); stream gradients take the dtype of the streams."""
 
         @staticmethod
         def forward(ctx, a, *xs):
             ys = fwd(list(xs), a)
             ctx.save_for_backward(a, *xs)
-            return tuple(y.to(xs[0].dtype) for y in ys)
+            return tuple(ys)
 
         @staticmethod
         def backward(ctx, *dys):

@@ -81,13 +81,18 @@ int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale,
             float* o, void* saved, size_t saved_bytes, void* stream);
 
 /* Backward pass: given dO, writes every gradient of the forward above in
- * float32: dq, dk, dv [T,H,d] and dc, dg [T,H].  Same inputs as ldc_fwd, plus
- * `saved` as written by ldc_fwd for these inputs (required; the backward
- * does not recompute the shared map).
- * workspace: device scratch of at least ldc_bwd_workspace_bytes(...) bytes
- * (16-byte aligned), owned by the caller; its contents on entry do not matter
- * and are undefined on return.  The pass is deterministic: equal inputs give
- * bitwise-equal outputs. */
+ * float32: dq, dk, dv [T,H,d] and dc, dg [T,H].  Same inputs as ldc_fwd, plus:
+ * saved: the state ldc_fwd wrote for these inputs (saved_bytes at least
+ *   ldc_saved_bytes(...)), or NULL: the pass then recomputes the shared map and
+ *   the softmax statistics from Q, K, C (the forward's score phase) into the
+ *   workspace first.
+ * workspace: device scratch, 16-byte aligned, owned by the caller.
+ *   ldc_bwd_workspace_bytes(...) bytes cover both cases; with `saved` given,
+ *   that size minus ldc_saved_bytes(...) rounded up to a multiple of 256 is
+ *   enough.  Its contents on entry do not matter and are undefined on return;
+ *   too small a workspace returns LDC_ERR_WORKSPACE.
+ * The pass is deterministic: equal inputs give bitwise-equal outputs, with or
+ * without `saved` (the recomputed state equals the saved one bit for bit). */
 int ldc_bwd(int dtype, int64_t T, int H, int d, int window, float scale,
             const void* q, const void* k, const void* v,
             const float* c, const float* g, const int32_t* doc_ids,
@@ -98,8 +103,10 @@ int ldc_bwd(int dtype, int64_t T, int H, int d, int window, float scale,
 /* The two kernels of ldc_bwd, callable one at a time (for per-kernel timing).
  * ldc_bwd is exactly ldc_bwd_q followed by ldc_bwd_kv with the same
  * arguments on the same stream:
- *   ldc_bwd_q  writes dq, dc, dg and dPbar (into the workspace);
- *   ldc_bwd_kv reads dc and the workspace and writes dk, dv.
+ *   ldc_bwd_q  writes dq, dc, dg and dPbar (into the workspace); with saved
+ *              NULL it first recomputes the saved state into the workspace;
+ *   ldc_bwd_kv reads dc and the workspace (and the saved state, or with saved
+ *              NULL the state ldc_bwd_q recomputed there) and writes dk, dv.
  * Arguments, validation and errors as for ldc_bwd; pointers the kernel does
  * not touch are still validated. */
 int ldc_bwd_q(int dtype, int64_t T, int H, int d, int window, float scale,
@@ -118,7 +125,8 @@ int ldc_bwd_kv(int dtype, int64_t T, int H, int d, int window, float scale,
 /* Bytes of the state ldc_fwd saves for ldc_bwd (0 for T == 0). */
 size_t ldc_saved_bytes(int dtype, int64_t T, int H, int d, int window);
 
-/* Bytes of workspace ldc_bwd needs for these sizes (0 for T == 0). */
+/* Bytes of workspace ldc_bwd needs for these sizes, with or without saved
+ * state (0 for T == 0 or unsupported sizes). */
 size_t ldc_bwd_workspace_bytes(int dtype, int64_t T, int H, int d, int window);
 
 /* Human-readable name of a status code (static storage). */

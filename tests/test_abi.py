@@ -40,10 +40,17 @@ def test_version_and_status_strings():
     assert "unknown" in ldc.status_str(99)
 
 
+def room(n):
+    return (n + 255) // 256 * 256
+
+
 def test_workspace_and_saved_bytes():
     band = 4096 * 2048 * 4  # 4,096 blocks of 16 queries x 2,048 words
-    assert ldc.workspace_bytes(ldc.LDC_BF16, 65536, 6, 128, 112) == band
-    assert ldc.saved_bytes(ldc.LDC_BF16, 65536, 6, 128, 112) == band + 65536 * 6 * 8
+    saved = band + 65536 * 6 * 8
+    assert ldc.saved_bytes(ldc.LDC_BF16, 65536, 6, 128, 112) == saved
+    # room for the recomputed saved state (when the caller passes none) + the dPbar band
+    assert ldc.workspace_bytes(ldc.LDC_BF16, 65536, 6, 128, 112) == room(saved) + band
+    assert ldc.workspace_bytes(ldc.LDC_F32, 17, 3, 16, 5) == room(2 * 8192 + 17 * 3 * 8) + 2 * 8192
     assert ldc.saved_bytes(ldc.LDC_F32, 17, 2, 16, 112) == 2 * 2048 * 4 + 17 * 2 * 8
     assert ldc.workspace_bytes(ldc.LDC_BF16, 0, 6, 128, 112) == 0
     assert ldc.workspace_bytes(ldc.LDC_BF16, 10, 6, 16, 112) == 0  # unsupported -> 0
@@ -101,10 +108,13 @@ def test_validation_errors(call):
 
 @pytest.mark.parametrize("entry", ["ldc_bwd", "ldc_bwd_q", "ldc_bwd_kv"])
 def test_bwd_workspace_errors(entry):
+    band = ldc.workspace_bytes(ldc.LDC_BF16, 256, 6, 128, 112) - room(ldc.saved_bytes(ldc.LDC_BF16, 256, 6, 128, 112))
+    assert band == 16 * 8192
     assert bwd_call(ws=None, entry=entry) == 6
     assert bwd_call(ws_bytes=100, entry=entry) == 6
+    assert bwd_call(ws_bytes=band - 16, entry=entry) == 6      # saved given: the band is enough
     assert bwd_call(ws=A + 4, entry=entry) == 4
-    assert bwd_call(saved=None, entry=entry) == 6
+    assert bwd_call(saved=None, ws_bytes=band, entry=entry) == 6  # no saved state: room for it too
     assert bwd_call(saved_bytes=100, entry=entry) == 6
     assert bwd_call(saved=A + 4, entry=entry) == 4
 

@@ -183,6 +183,77 @@ def test_autograd_function(ldc):
         assert_close("d" + name, to_np(ts[name].grad), ref, "f32")
 
 
+def test_autograd_function_bf16(ldc):
+    """ldc_attention on bf16 inputs: O comes back in float32 and meets the bf16
+    bar; the gradients of the bf16 leaves are the kernels' float32 gradients
+    rounded to bf16 by autograd (a leaf's gradient takes the leaf's dtype), and
+    still meet the bf16 bar; C and G are float32 leaves."""
+    import torch
+    w = wl.make_workload(384, 6, 128, dtype="bf16", seed=31, docs=("geometric", 150))
+    x = w.torch_inputs("cuda")
+    ts = {kk: x[kk].clone().requires_grad_(True) for kk in ("q", "k", "v", "c", "g")}
+    o = ldc.ldc_attention(ts["q"], ts["k"], ts["v"], ts["c"], ts["g"], x["doc"], w.window, w.scale)
+    assert o.dtype == torch.float32
+    o.backward(x["do"].float())
+    ref_o = orc.forward(w.q, w.k, w.v, w.c, w.g, w.doc, window=w.window, scale=w.scale)
+    assert_close("o", to_np(o), ref_o, "bf16")
+    gr = orc.backward(w.q, w.k, w.v, w.c, w.g, w.doc, w.do, window=w.window, scale=w.scale)
+    for name, ref in zip(("q", "k", "v", "c", "g"), gr):
+        assert ts[name].grad.dtype == ts[name].dtype
+        assert_close("d" + name, to_np(ts[name].grad), ref, "bf16")
+
+
+def test_explicit_stream_argument(ldc):
+    """stream= passed outside a stream context: the calls allocate their
+    outputs, saved state and workspace on that stream and give the
+    default-stream result bit for bit."""
+    import torch
+    w = wl.make_workload(600, 6, 128, dtype="bf16", seed=27)
+    ref, _ = run_gpu(ldc, w)
+    x = w.torch_inputs("cuda", with_do=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    args = (x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"])
+    o, saved = ldc.fwd(*args, window=w.window, scale=w.scale, save=True, stream=s)
+    grads = ldc.bwd(*args, saved, x["do"], window=w.window, scale=w.scale, stream=s)
+    # more allocations on the current stream while s may still run
+    junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(8)]
+    s.synchronize()
+    del junk
+    assert torch.equal(o, ref["o"])
+    for name, gr in zip(GRADS, grads):
+        assert torch.equal(gr, ref[name]), name
+
+
+def test_kv_part_needs_workspace(ldc):
+    w = wl.make_workload(64, 2, 64, dtype="bf16", seed=28)
+    x = w.torch_inputs("cuda", with_do=True)
+    args = (x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"])
+    _, saved = ldc.fwd(*args, save=True)
+    with pytest.raises(ValueError):
+        ldc.bwd(*args, saved, x["do"], part="kv")
+
+
+@pytest.mark.parametrize("T,H,d,dtype,window", [(700, 6, 128, "bf16", 112), (300, 3, 64, "f32", 37),
+                                                  (1000, 12, 64, "bf16", 112)])
+def test_backward_without_saved_state(ldc, T, H, d, dtype, window):
+    """ldc_bwd with saved = NULL recomputes the shared map and statistics
+    (the forward's score phase) into its workspace: the gradients equal the
+    call with the forward's saved state bit for bit, and the oracle's."""
+    import torch
+    w = wl.make_workload(T, H, d, dtype=dtype, window=window, seed=29, docs=("geometric", 150))
+    x = w.torch_inputs("cuda", with_do=True)
+    args = (x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"])
+    _, saved = ldc.fwd(*args, window=w.window, scale=w.scale, save=True)
+    with_state = ldc.bwd(*args, saved, x["do"], window=w.window, scale=w.scale)
+    without = ldc.bwd(*args, None, x["do"], window=w.window, scale=w.scale)
+    torch.cuda.synchronize()
+    ref = orc.backward(w.q, w.k, w.v, w.c, w.g, w.doc, w.do, window=w.window, scale=w.scale)
+    for name, a_, b_, r in zip(GRADS, with_state, without, ref):
+        assert torch.equal(a_, b_), name
+        assert_close(name, to_np(b_), r, w.dtype)
+
+
 def test_split_backward_matches(ldc):
     """ldc_bwd_q then ldc_bwd_kv on one workspace gives exactly ldc_bwd."""
     import torch
