@@ -272,6 +272,33 @@ def test_split_backward_matches(ldc):
         assert torch.equal(a_, b_), name
 
 
+@pytest.mark.parametrize("T,H,d,dtype,seed", [(8192, 6, 128, "bf16", 51), (5000, 12, 64, "bf16", 52),
+                                              (2000, 3, 64, "f32", 53), (700, 2, 128, "f32", 54)])
+def test_backward_whole_tensor(ldc, T, H, d, dtype, seed):
+    """Every gradient over the whole stream against the oracle, for streams of
+    many tiles (64 of 128 tokens, 63 of 64 tokens at 12 x 64 and float32)."""
+    w = wl.make_workload(T, H, d, dtype=dtype, seed=seed, docs=("geometric", 300))
+    check_all(ldc, w)
+
+
+def test_workspace_reuse(ldc):
+    """Back-to-back calls on one workspace, with and without saved state,
+    give identical results."""
+    import torch
+    w = wl.make_workload(3000, 6, 128, dtype="bf16", seed=55)
+    x = w.torch_inputs("cuda", with_do=True)
+    args = (x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"])
+    _, saved = ldc.fwd(*args, window=w.window, scale=w.scale, save=True)
+    ws = torch.empty(ldc.workspace_bytes(ldc.LDC_BF16, 3000, 6, 128, w.window), dtype=torch.uint8,
+                     device="cuda")
+    r1 = ldc.bwd(*args, saved, x["do"], window=w.window, scale=w.scale, workspace=ws)
+    r2 = ldc.bwd(*args, saved, x["do"], window=w.window, scale=w.scale, workspace=ws)
+    r3 = ldc.bwd(*args, None, x["do"], window=w.window, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    for name, a_, b_, c_ in zip(GRADS, r1, r2, r3):
+        assert torch.equal(a_, b_) and torch.equal(a_, c_), name
+
+
 def test_custom_scale(ldc):
     """A softmax scale other than 1/sqrt(d) is honoured by both passes."""
     w = wl.make_workload(300, 2, 128, dtype="bf16", seed=25, scale=0.37)
