@@ -22,7 +22,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["fwd", "bwd", "ldc_attention", "LDCFunction", "LDCError", "load_library",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "noalloc_max_workspace", "ldc_attention", "LDCFunction", "LDCError", "load_library",
            "workspace_bytes", "saved_bytes", "status_str", "version", "LIB_PATH",
            "LDC_BF16", "LDC_F32"]
 
@@ -56,6 +56,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         getattr(lib, nm).argtypes = ([i32, i64, i32, i32, i32, f32] + [vp] * 6 + [vp, sz]
                                      + [vp] * 6 + [vp, sz, vp])
         getattr(lib, nm).restype = i32
+    lib.ldc_bwd_noalloc.argtypes = ([i32, i64, i32, i32, i32, f32] + [vp] * 6 + [vp, sz]
+                                    + [vp] * 6 + [vp])
+    lib.ldc_bwd_noalloc.restype = i32
+    lib.ldc_bwd_noalloc_max_workspace.argtypes = []
+    lib.ldc_bwd_noalloc_max_workspace.restype = sz
     for nm in ("ldc_bwd_workspace_bytes", "ldc_saved_bytes"):
         getattr(lib, nm).argtypes = [i32, i64, i32, i32, i32]
         getattr(lib, nm).restype = sz
@@ -187,6 +192,7 @@ def bwd(q, k, v, c, g, doc_ids, saved, do, window: int = DEFAULT_WINDOW,
         if workspace is None:
             need = workspace_bytes(_dtype_code(q), T, H, d, window)
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_grads(out, T, H, d, q.device)
     dq, dk, dv, dc, dg = out
     sp, sn = _buf(saved)
     wp, wn = _buf(workspace)
@@ -199,6 +205,46 @@ def bwd(q, k, v, c, g, doc_ids, saved, do, window: int = DEFAULT_WINDOW,
     if st != 0:
         raise LDCError(st, {"all": "ldc_bwd", "q": "ldc_bwd_q", "kv": "ldc_bwd_kv"}[part])
     return dq, dk, dv, dc, dg
+
+
+def _check_grads(out, T, H, d, device):
+    torch = _torch()
+    if out is None or len(out) != 5:
+        raise ValueError("out must be the five gradient tensors (dq, dk, dv, dc, dg)")
+    for name, x, shape in zip(("dq", "dk", "dv", "dc", "dg"), out,
+                              ((T, H, d),) * 3 + ((T, H),) * 2):
+        if (tuple(x.shape) != shape or x.dtype != torch.float32 or not x.is_contiguous()
+                or x.device != device):
+            raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor on {device}")
+
+
+def bwd_noalloc(q, k, v, c, g, doc_ids, saved, do, out, window: int = DEFAULT_WINDOW,
+                scale: Optional[float] = None, stream=None):
+    """ldc_bwd without a caller workspace and without any allocation: the
+    library's static per-GPU scratch serves as workspace (ldc_bwd_noalloc).
+    `out` = (dq, dk, dv, dc, dg) must be given.  Calls that overlap on one GPU
+    race on the scratch: keep them on one stream."""
+    torch = _torch()
+    lib = load_library()
+    T, H, d = _check(q, k, v, c, g, doc_ids, do)
+    _check_grads(out, T, H, d, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st_obj = torch.cuda.current_stream(q.device) if stream is None else stream
+    dq, dk, dv, dc, dg = out
+    sp, sn = _buf(saved)
+    st = lib.ldc_bwd_noalloc(_dtype_code(q), T, H, d, window, float(scale),
+                             q.data_ptr(), k.data_ptr(), v.data_ptr(), c.data_ptr(), g.data_ptr(),
+                             doc_ids.data_ptr(), sp, sn, do.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dc.data_ptr(),
+                             dg.data_ptr(), ctypes.c_void_p(st_obj.cuda_stream))
+    if st != 0:
+        raise LDCError(st, "ldc_bwd_noalloc")
+    return out
+
+
+def noalloc_max_workspace() -> int:
+    return int(load_library().ldc_bwd_noalloc_max_workspace())
 
 
 def _make_function():

@@ -47,6 +47,9 @@ const char* ldc_status_str(int status) {
     case LDC_ERR_UNSUPPORTED: return "LDC_ERR_UNSUPPORTED: head dim not available for this dtype";
     case LDC_ERR_WORKSPACE: return "LDC_ERR_WORKSPACE: workspace missing or too small";
     case LDC_ERR_HIP: return "LDC_ERR_HIP: a HIP launch failed";
+    case LDC_ERR_SCRATCH:
+      return "LDC_ERR_SCRATCH: the call needs more workspace than ldc_bwd_noalloc's static scratch "
+             "(ldc_bwd_noalloc_max_workspace() bytes)";
     default: return "unknown ldc status";
   }
 }
@@ -91,14 +94,17 @@ int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale, const v
   return e == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
 
-static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, float scale,
-                     const void* q, const void* k, const void* v, const float* c, const float* g,
-                     const int32_t* doc_ids, const void* saved, size_t saved_bytes, const void* dO,
-                     float* dq, float* dk, float* dv, float* dc, float* dg, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+// Validation shared by the backward entry points (everything but the
+// workspace).  On LDC_OK, *need_ws holds the workspace bytes the call needs.
+static int bwd_validate(int dtype, int64_t T, int H, int d, int window, float scale,
+                        const void* q, const void* k, const void* v, const float* c,
+                        const float* g, const int32_t* doc_ids, const void* saved,
+                        size_t saved_bytes, const void* dO, float* dq, float* dk, float* dv,
+                        float* dc, float* dg, size_t* need_ws) {
   int st = check_common(dtype, T, H, d, window);
   if (st != LDC_OK) return st;
   if (!scale_ok(scale)) return LDC_ERR_SHAPE;
+  *need_ws = 0;
   if (T == 0) return LDC_OK;
   const void* ptrs[] = {q, k, v, c, g, doc_ids, dO, dq, dk, dv, dc, dg};
   for (const void* p : ptrs)
@@ -111,11 +117,16 @@ static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, 
     if (!aligned16(saved)) return LDC_ERR_ALIGN;
   }
   // Without saved state the workspace first holds the recomputed state.
-  const size_t need_ws = (saved ? 0 : state_room(need_saved)) + bwd_own_bytes(T);
-  if (!workspace || workspace_bytes < need_ws) return LDC_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return LDC_ERR_ALIGN;
-  char* ws = static_cast<char*>(workspace);
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  *need_ws = (saved ? 0 : state_room(need_saved)) + bwd_own_bytes(T);
+  return LDC_OK;
+}
+
+// Enqueues the backward kernels on validated arguments and a large enough workspace.
+static int bwd_run(int parts, int dtype, int64_t T, int H, int d, int window, float scale,
+                   const void* q, const void* k, const void* v, const float* c, const float* g,
+                   const int32_t* doc_ids, const void* saved, const void* dO, float* dq,
+                   float* dk, float* dv, float* dc, float* dg, char* ws, hipStream_t hs) {
+  const size_t need_saved = ldc_saved_bytes(dtype, T, H, d, window);
   const void* state = saved;
   if (!saved) {
     state = ws;
@@ -139,6 +150,21 @@ static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, 
   return e == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
 
+static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, float scale,
+                     const void* q, const void* k, const void* v, const float* c, const float* g,
+                     const int32_t* doc_ids, const void* saved, size_t saved_bytes, const void* dO,
+                     float* dq, float* dk, float* dv, float* dc, float* dg, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  size_t need_ws = 0;
+  int st = bwd_validate(dtype, T, H, d, window, scale, q, k, v, c, g, doc_ids, saved, saved_bytes,
+                        dO, dq, dk, dv, dc, dg, &need_ws);
+  if (st != LDC_OK || T == 0) return st;
+  if (!workspace || workspace_bytes < need_ws) return LDC_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LDC_ERR_ALIGN;
+  return bwd_run(parts, dtype, T, H, d, window, scale, q, k, v, c, g, doc_ids, saved, dO, dq, dk,
+                 dv, dc, dg, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
 #define LDC_BWD_PARAMS                                                                          \
   int dtype, int64_t T, int H, int d, int window, float scale, const void *q, const void *k,    \
       const void *v, const float *c, const float *g, const int32_t *doc_ids, const void *saved, \
@@ -151,5 +177,26 @@ static int bwd_parts(int parts, int dtype, int64_t T, int H, int d, int window, 
 int ldc_bwd(LDC_BWD_PARAMS) { return bwd_parts(3, LDC_BWD_ARGS); }
 int ldc_bwd_q(LDC_BWD_PARAMS) { return bwd_parts(1, LDC_BWD_ARGS); }
 int ldc_bwd_kv(LDC_BWD_PARAMS) { return bwd_parts(2, LDC_BWD_ARGS); }
+
+int ldc_bwd_noalloc(int dtype, int64_t T, int H, int d, int window, float scale, const void* q,
+                    const void* k, const void* v, const float* c, const float* g,
+                    const int32_t* doc_ids, const void* saved, size_t saved_bytes, const void* dO,
+                    float* dq, float* dk, float* dv, float* dc, float* dg, void* stream) {
+  size_t need_ws = 0;
+  int st = bwd_validate(dtype, T, H, d, window, scale, q, k, v, c, g, doc_ids, saved, saved_bytes,
+                        dO, dq, dk, dv, dc, dg, &need_ws);
+  if (st != LDC_OK || T == 0) return st;
+  if (need_ws > ldc::kStaticScratchBytes) return LDC_ERR_SCRATCH;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  // The stream's device decides which copy of the static scratch the kernels use.
+  int dev = 0;
+  if (hipStreamGetDevice(hs, &dev) != hipSuccess) return LDC_ERR_HIP;
+  void* ws = nullptr;
+  if (ldc::static_scratch(dev, &ws) != hipSuccess) return LDC_ERR_HIP;
+  return bwd_run(3, dtype, T, H, d, window, scale, q, k, v, c, g, doc_ids, saved, dO, dq, dk, dv,
+                 dc, dg, static_cast<char*>(ws), hs);
+}
+
+size_t ldc_bwd_noalloc_max_workspace(void) { return ldc::kStaticScratchBytes; }
 
 }  // extern "C"

@@ -26,6 +26,8 @@
 #include "ldc_internal.h"
 #include "ldc_pipeline.hpp"
 
+#include <mutex>
+
 namespace ldc {
 
 // ---------------------------------------------------------------------------
@@ -540,6 +542,36 @@ hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, int parts, hipStream
     if (d == 16) return launch_bwd<float, 16, 4>(a, parts, st);
   }
   return hipErrorInvalidValue;
+}
+
+// Workspace of the allocation-free backward entry point: one array per GPU,
+// held by the loaded code object until the process ends.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(int device, void** ptr) {
+  // The host-side name of `scratch` is not a device address: the device
+  // address is asked for once per device, with that device current.
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 }  // namespace ldc

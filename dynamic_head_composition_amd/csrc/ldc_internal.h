@@ -40,4 +40,10 @@ hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, bool value, hipStrea
 // parts: bit 0 = query-side kernel, bit 1 = key-side kernel
 hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, int parts, hipStream_t st);
 
+// Static device workspace of ldc_bwd_noalloc (bytes per GPU) and the device
+// address of one GPU's copy (looked up on first use, then cached).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(int device, void** ptr);
+
 }  // namespace ldc

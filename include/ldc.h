@@ -30,8 +30,9 @@
  *
  * Execution: work is enqueued on `stream` (a hipStream_t; NULL = the default
  * stream) and the call returns without synchronising.  The library allocates
- * nothing, keeps no global state and is reentrant.  Outputs are fully
- * overwritten (no accumulate mode).
+ * no device memory; apart from the static scratch of ldc_bwd_noalloc it keeps
+ * no global state, and every other entry point is reentrant.  Outputs are
+ * fully overwritten (no accumulate mode).
  *
  * Errors: arguments are validated before any HIP call; a validation failure
  * returns a non-zero ldc_status and has no side effects.  A failed kernel
@@ -56,7 +57,8 @@ typedef enum {
   LDC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned              */
   LDC_ERR_UNSUPPORTED = 5, /* head dim not instantiated for this dtype      */
   LDC_ERR_WORKSPACE = 6,   /* saved state / workspace missing or too small  */
-  LDC_ERR_HIP = 7          /* a HIP launch failed                           */
+  LDC_ERR_HIP = 7,         /* a HIP launch failed                           */
+  LDC_ERR_SCRATCH = 8      /* ldc_bwd_noalloc: problem exceeds its scratch  */
 } ldc_status;
 
 typedef enum {
@@ -121,6 +123,32 @@ int ldc_bwd_kv(int dtype, int64_t T, int H, int d, int window, float scale,
                const void* saved, size_t saved_bytes, const void* dO,
                float* dq, float* dk, float* dv, float* dc, float* dg,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ldc_bwd
+ * without the workspace arguments.  Its workspace is a static device array of
+ * ldc_bwd_noalloc_max_workspace() bytes (64 MiB) per GPU, part of the loaded
+ * library and held until the process ends; the first call on a GPU looks up
+ * that GPU's copy (a HIP call that allocates nothing).  The GPU is the one
+ * `stream` belongs to.  Nothing in it must start at zero: each call writes
+ * every word it later reads.
+ * Other arguments, validation, errors and results as for ldc_bwd (results are
+ * bitwise equal to ldc_bwd's on the same inputs).  A call whose workspace
+ * (ldc_bwd_workspace_bytes minus the room for saved state when `saved` is
+ * given, as for ldc_bwd) exceeds the scratch returns LDC_ERR_SCRATCH: with
+ * saved state that allows T up to 131,072 tokens; without, about
+ * 64 MiB / (1,024 + 8*H) bytes per token.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (concurrent streams, or host threads) race and give undefined results;
+ * serialise them on one stream. */
+int ldc_bwd_noalloc(int dtype, int64_t T, int H, int d, int window, float scale,
+                    const void* q, const void* k, const void* v,
+                    const float* c, const float* g, const int32_t* doc_ids,
+                    const void* saved, size_t saved_bytes, const void* dO,
+                    float* dq, float* dk, float* dv, float* dc, float* dg, void* stream);
+
+/* Size in bytes of ldc_bwd_noalloc's static scratch (per GPU). */
+size_t ldc_bwd_noalloc_max_workspace(void);
 
 /* Bytes of the state ldc_fwd saves for ldc_bwd (0 for T == 0). */
 size_t ldc_saved_bytes(int dtype, int64_t T, int H, int d, int window);

@@ -24,8 +24,9 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = ldc.load_library()
     names = declared_functions()
-    assert names == ["ldc_bwd", "ldc_bwd_kv", "ldc_bwd_q", "ldc_bwd_workspace_bytes", "ldc_fwd",
-                     "ldc_saved_bytes", "ldc_status_str", "ldc_version"]
+    assert names == ["ldc_bwd", "ldc_bwd_kv", "ldc_bwd_noalloc", "ldc_bwd_noalloc_max_workspace",
+                     "ldc_bwd_q", "ldc_bwd_workspace_bytes", "ldc_fwd", "ldc_saved_bytes",
+                     "ldc_status_str", "ldc_version"]
     for nm in names:
         assert hasattr(lib, nm)
     out = subprocess.run(["nm", "-D", "--defined-only", ldc.LIB_PATH], capture_output=True, text=True).stdout
@@ -35,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert ldc.version() == 10000
-    for code in range(8):
+    for code in range(9):
         assert ldc.status_str(code).startswith("LDC_")
     assert "unknown" in ldc.status_str(99)
 
@@ -75,6 +76,15 @@ def bwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, ws=A,
                                ws, ws_bytes, None)
 
 
+def bwd_noalloc_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, saved=A,
+                     saved_bytes=None, scale=0.1):
+    lib = ldc.load_library()
+    p = ptrs or [A] * 12
+    if saved_bytes is None:
+        saved_bytes = ldc.saved_bytes(dtype, T, H, d, window)
+    return lib.ldc_bwd_noalloc(dtype, T, H, d, window, scale, *p[:6], saved, saved_bytes, *p[6:], None)
+
+
 def bwd_q_call(**kw):
     return bwd_call(entry="ldc_bwd_q", **kw)
 
@@ -83,7 +93,7 @@ def bwd_kv_call(**kw):
     return bwd_call(entry="ldc_bwd_kv", **kw)
 
 
-@pytest.mark.parametrize("call", [fwd_call, bwd_call, bwd_q_call, bwd_kv_call])
+@pytest.mark.parametrize("call", [fwd_call, bwd_call, bwd_q_call, bwd_kv_call, bwd_noalloc_call])
 def test_validation_errors(call):
     assert call(dtype=2) == 3                      # LDC_ERR_DTYPE
     assert call(T=-1) == 2                         # LDC_ERR_SHAPE
@@ -117,6 +127,21 @@ def test_bwd_workspace_errors(entry):
     assert bwd_call(saved=None, ws_bytes=band, entry=entry) == 6  # no saved state: room for it too
     assert bwd_call(saved_bytes=100, entry=entry) == 6
     assert bwd_call(saved=A + 4, entry=entry) == 4
+
+
+def test_noalloc_scratch_limit():
+    """ldc_bwd_noalloc refuses, before any HIP call, a problem whose workspace
+    exceeds its 64 MiB static scratch; other errors come first."""
+    lib = ldc.load_library()
+    assert lib.ldc_bwd_noalloc_max_workspace() == 64 << 20
+    # with saved state the workspace is the dPbar band, 512 bytes per token
+    assert bwd_noalloc_call(T=131073, H=1, d=16, dtype=ldc.LDC_F32) == 8       # LDC_ERR_SCRATCH
+    # without, it also holds the recomputed state
+    assert bwd_noalloc_call(T=65536, H=6, saved=None, saved_bytes=0) == 8
+    assert bwd_noalloc_call(T=131073, H=1, d=16, dtype=ldc.LDC_F32, saved_bytes=100) == 6
+    assert bwd_noalloc_call(T=131073, H=1, d=16, dtype=ldc.LDC_F32, saved=A + 4) == 4
+    assert lib.ldc_bwd_noalloc(0, 0, 6, 128, 112, 0.1, *([None] * 6), None, 0, *([None] * 6), None) == 0
+    assert "static scratch" in ldc.status_str(8)
 
 
 def test_fwd_saved_errors():
