@@ -68,6 +68,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ldc_status_str.restype = ctypes.c_char_p
     lib.ldc_version.argtypes = []
     lib.ldc_version.restype = i32
+    lib.dcmha_fwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 7 + [vp, sz, vp]
+    lib.dcmha_fwd.restype = i32
+    for nm in ("dcmha_bwd", "dcmha_bwd_q", "dcmha_bwd_kv"):
+        getattr(lib, nm).argtypes = ([i32, i64, i32, i32, i32, f32] + [vp] * 6 + [vp, sz]
+                                     + [vp] * 6 + [vp, sz, vp])
+        getattr(lib, nm).restype = i32
+    for nm in ("dcmha_saved_bytes", "dcmha_bwd_workspace_bytes"):
+        getattr(lib, nm).argtypes = [i32, i64, i32, i32, i32]
+        getattr(lib, nm).restype = sz
     lib.mudd_fwd.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp, vp]
     lib.mudd_fwd.restype = i32
     lib.mudd_bwd.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]

@@ -254,6 +254,108 @@ def config_workload(i: int, T: Optional[int] = None) -> Workload:
 
 
 # ----------------------------------------------------------------------------
+# Full DCMHA composition (AITNT page, section "第二刀-砍层内", DCMHA paragraph)
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class DcmhaWorkload:
+    name: str
+    T: int
+    H: int
+    d: int
+    window: int
+    dtype: str
+    scale: float
+    q: np.ndarray       # [T, H, d] float32 (values representable in `dtype`)
+    k: np.ndarray
+    v: np.ndarray
+    cs: np.ndarray      # [T, H, H] float32 score composition
+    cw: np.ndarray      # [T, H, H] float32 weight composition
+    doc: np.ndarray     # [T] int32
+    do: np.ndarray      # [T, H, d] float32 (representable in `dtype`)
+    recipe: str = ""
+
+    def torch_inputs(self, device="cuda"):
+        import torch
+
+        def big(x):
+            if self.dtype == "bf16":
+                return torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(device)
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+        f = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(device)
+        return dict(q=big(self.q), k=big(self.k), v=big(self.v), cs=f(self.cs), cw=f(self.cw),
+                    doc=f(self.doc), do=big(self.do))
+
+
+def _composition(rng, kind: str, T: int, H: int) -> np.ndarray:
+    """[T, H, H] per-query head compositions.
+    "eye+normal0.3": I + N(0, 0.3^2) (each head keeps mostly its own map, mixed
+                     with every other head's, either sign);
+    "eye":           the identity;
+    "perm":          a random permutation matrix per query."""
+    if kind == "eye+normal0.3":
+        return (np.eye(H, dtype=np.float32)[None] + 0.3 * _normal(rng, (T, H, H))).astype(np.float32)
+    if kind == "eye":
+        return np.broadcast_to(np.eye(H, dtype=np.float32)[None], (T, H, H)).copy()
+    if kind == "perm":
+        out = np.zeros((T, H, H), dtype=np.float32)
+        for t in range(T):
+            out[t, np.arange(H), rng.permutation(H)] = 1.0
+        return out
+    raise ValueError(kind)
+
+
+def make_dcmha_workload(T: int, H: int, d: int, *, window: int = WINDOW, dtype: str = "bf16",
+                        seed: int = 0, docs=("geometric", 1024), qk_rms: bool = True,
+                        cs_kind: str = "eye+normal0.3", cw_kind: str = "eye+normal0.3",
+                        scale: Optional[float] = None, name: Optional[str] = None) -> DcmhaWorkload:
+    """Seeded DCMHA workload.  Draw order (one PCG64 stream): document lengths,
+    Q, K, V, CS, CW, dO; Q, K, V, dO rounded to bf16 (RNE) for bf16 workloads.
+    cs_kind / cw_kind as in _composition; cw_kind "ldc" takes G[t,h] C[t,:]
+    with C ~ N(0, 0.5^2), G ~ U(0.5, 1.5) (the Lightweight DC layer's weights,
+    drawn C then G)."""
+    assert dtype in ("bf16", "f32")
+    rng = np.random.default_rng(seed)
+    kind = docs[0]
+    if kind == "geometric":
+        doc = geometric_docs(rng, T, docs[1])
+    elif kind == "uniform":
+        doc = uniform_docs(rng, T, docs[1], docs[2])
+    elif kind == "single":
+        doc = np.zeros(T, dtype=np.int32)
+    else:
+        raise ValueError(kind)
+    rnd = round_bf16 if dtype == "bf16" else (lambda x: x)
+    q = _normal(rng, (T, H, d))
+    k = _normal(rng, (T, H, d))
+    if qk_rms:
+        q, k = _rms_rows(q), _rms_rows(k)
+    q, k = rnd(q), rnd(k)
+    v = rnd(_normal(rng, (T, H, d)))
+    cs = _composition(rng, cs_kind, T, H)
+    if cw_kind == "ldc":
+        c = (0.5 * _normal(rng, (T, H))).astype(np.float32)
+        g = rng.uniform(0.5, 1.5, size=(T, H)).astype(np.float32)
+        cw = (g[:, :, None] * c[:, None, :]).astype(np.float32)
+    else:
+        cw = _composition(rng, cw_kind, T, H)
+    do = rnd(_normal(rng, (T, H, d)))
+    return DcmhaWorkload(name=name or f"dcmha_T{T}_H{H}_d{d}_{dtype}_s{seed}", T=T, H=H, d=d,
+                         window=window, dtype=dtype,
+                         scale=(1.0 / math.sqrt(d)) if scale is None else float(scale),
+                         q=q, k=k, v=v, cs=cs, cw=cw, doc=doc, do=do,
+                         recipe=f"docs={docs[0]}{tuple(docs[1:])} qk_rms={qk_rms} CS={cs_kind} "
+                                f"CW={cw_kind} seed={seed}")
+
+
+# The DCMHA benchmark workload: the GPT-2 small attention shape of the
+# Lightweight DC configurations, forward+backward.
+DCMHA_BENCH = dict(T=65536, H=6, d=128, dtype="bf16", seed=5, docs=("geometric", 1024),
+                   cs_kind="eye+normal0.3", cw_kind="eye+normal0.3",
+                   name="dcmha_gpt2s_fwdbwd_T65536_H6_d128")
+
+
+# ----------------------------------------------------------------------------
 # MUDD layer mixing (AITNT page, section "第一刀—砍层间")
 # ----------------------------------------------------------------------------
 @dataclasses.dataclass
