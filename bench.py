@@ -25,6 +25,10 @@ is seeded and synthetic; it stands in for the FineWeb token stream the
 speedrun trains on.  The CPU baseline times the fp64 oracle on the host cores
 over a bounded leading part of the same stream.
 
+With --workload dcmha the step is the full DCMHA composition layer (score and
+weight compositions across heads, dcmha_fwd + dcmha_bwd_q + dcmha_bwd_kv) at
+the same GPT-2 small shape, reported in the same format.
+
 With --workload mudd the step is one MUDD mix forward and backward
 (mudd_fwd + mudd_bwd) over a GPT-2 small token stream (65,536 tokens, model
 dim 768, 13 layer streams, 4 ways), reported in the same format.
@@ -229,6 +233,173 @@ def mudd_cpu_baseline(w, budget_s: float, chunk: int = 2048):
                       f"in {chunk}-token slices; {el:.1f} s"}
 
 
+DCMHA_METRIC = "DCMHA composition attention fwd+bwd tokens/s on 1 MI355X (GPT-2-small shape)"
+DCMHA_KERNELS = ("dcmha_fwd", "dcmha_bwd_q", "dcmha_bwd_kv")
+DCMHA_PASSES = {"dcmha_fwd": ("dcmha_fwd",), "dcmha_bwd": ("dcmha_bwd_q", "dcmha_bwd_kv")}
+DCMHA_SOURCES = ("ldc_device.hpp", "ldc_pipeline.hpp", "dcmha.hip", "dcmha_internal.h")
+
+
+def dcmha_spec_bytes_per_token(H: int, d: int, elem: int) -> dict:
+    """Compulsory HBM bytes per token of each DCMHA pass (every tensor of the
+    definition once, O in the storage dtype): forward Q, K, V, CS, CW, doc in,
+    O out; backward Q, K, V, dO, CS, CW, doc in, dQ, dK, dV (float32), dCS,
+    dCW out."""
+    row, comp = H * d, 4 * H * H
+    return {"dcmha_fwd": 3 * row * elem + 2 * comp + 4 + row * elem,
+            "dcmha_bwd": 4 * row * elem + 2 * comp + 4 + 3 * row * 4 + 2 * comp}
+
+
+def dcmha_design_bytes_per_token(H: int, d: int, elem: int) -> dict:
+    """Bytes per token each DCMHA kernel moves as designed: its operands once,
+    float32 O and gradients, and the per-head bands the kernels hand each
+    other (512 B per token and head each): P and R saved by the forward, P
+    read twice by bwd_q (the mixing passes), dS written by bwd_q and read by
+    bwd_kv with R."""
+    row, comp, band = H * d, 4 * H * H, 512 * H
+    return {
+        "dcmha_fwd": 3 * row * elem + 2 * comp + 4 + row * 4 + 2 * band,
+        "dcmha_bwd_q": 4 * row * elem + 2 * comp + 4 + 2 * band + row * 4 + 2 * comp + band,
+        "dcmha_bwd_kv": 2 * row * elem + 4 + 2 * band + 2 * row * 4,
+    }
+
+
+def dcmha_cpu_baseline(w, budget_s: float, chunk: int = 256):
+    """Time the fp64 DCMHA oracle (forward + backward) on leading slices of
+    the stream (each with its window halo) until `budget_s` seconds."""
+    from oracle import dcmha_oracle as dco
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.T and time.perf_counter() - t0 < budget_s:
+        lo, hi = done, min(w.T, done + chunk)
+        a0 = max(0, lo - w.window + 1)
+        sl = lambda x: x[a0:hi]
+        qs = range(lo - a0, hi - a0)
+        dco.forward(sl(w.q), sl(w.k), sl(w.v), sl(w.cs), sl(w.cw), sl(w.doc), window=w.window,
+                    scale=w.scale, queries=qs)
+        dco.backward(sl(w.q), sl(w.k), sl(w.v), sl(w.cs), sl(w.cw), sl(w.doc), sl(w.do),
+                     window=w.window, scale=w.scale)
+        done = hi
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            **host_cpu(),
+            "sample": f"fp64 DCMHA oracle forward (the slice's queries) + backward (the slice with its "
+                      f"{w.window - 1}-token halo) over tokens [0, {done}) of the same stream in "
+                      f"{chunk}-token slices; {el:.1f} s"}
+
+
+def bench_dcmha(args):
+    import torch
+    import dynamic_head_composition_amd as ldc
+    from dynamic_head_composition_amd import dcmha
+    from dynamic_head_composition_amd import workloads as wl
+
+    ldc.load_library()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    cfg = dict(wl.DCMHA_BENCH)
+    if args.tokens:
+        cfg["T"] = args.tokens
+        cfg["name"] += f"_trunc{args.tokens}"
+    log(f"generating DCMHA workload {cfg} ...")
+    w = wl.make_dcmha_workload(**cfg)
+    x = w.torch_inputs("cuda")
+    T, H, d = w.T, w.H, w.d
+    elem = 2 if w.dtype == "bf16" else 4
+    code = ldc.LDC_BF16 if w.dtype == "bf16" else ldc.LDC_F32
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o = torch.empty((T, H, d), **f32)
+    grads = tuple(torch.empty(s, **f32) for s in ((T, H, d),) * 3 + ((T, H, H),) * 2)
+    ws = torch.empty(max(16, dcmha.workspace_bytes(code, T, H, d, w.window)), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(max(16, dcmha.saved_bytes(code, T, H, d, w.window)), dtype=torch.uint8, device="cuda")
+    ins = (x["q"], x["k"], x["v"], x["cs"], x["cw"], x["doc"])
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        dcmha.fwd(*ins, window=w.window, scale=w.scale, out=o, saved=saved)
+        if evs:
+            evs[1].record()
+        dcmha.bwd(*ins, saved, x["do"], window=w.window, scale=w.scale, out=grads, workspace=ws, part="q")
+        if evs:
+            evs[2].record()
+        dcmha.bwd(*ins, saved, x["do"], window=w.window, scale=w.scale, out=grads, workspace=ws, part="kv")
+        if evs:
+            evs[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if not all(bool(torch.isfinite(t).all()) for t in (o,) + grads):
+        raise SystemExit("non-finite outputs")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    span = lambda a_, b_: [evs[i][a_].elapsed_time(evs[i][b_]) for i in range(args.steps)]
+    kstat = {kn: stats_us(span(j, j + 1)) for j, kn in enumerate(DCMHA_KERNELS)}
+    pstat = {"dcmha_fwd": stats_us(span(0, 1)), "dcmha_bwd": stats_us(span(1, 3))}
+    spec = dcmha_spec_bytes_per_token(H, d, elem)
+    design = dcmha_design_bytes_per_token(H, d, elem)
+    passes = {}
+    for pn, kernels in DCMHA_PASSES.items():
+        sec = pstat[pn]["median_us"] * 1e-6
+        alg = spec[pn] * T
+        traffic = measured_traffic(kernels, w.name, DCMHA_SOURCES)
+        passes[pn] = {**pstat[pn], "kernels": list(kernels), "alg_bytes_per_launch": alg,
+                      "alg_GBps": round(alg / sec / 1e9, 1), "frac": round(alg / sec / 1e9 / HBM_PEAK_GBPS, 4),
+                      "design_bytes_per_launch": sum(design[kn] for kn in kernels) * T,
+                      "traffic": traffic,
+                      "traffic_over_alg": None if traffic is None else round(traffic / alg, 3)}
+    per_kernel = {kn: {**kstat[kn], "design_bytes_per_launch": design[kn] * T,
+                       "design_GBps": round(design[kn] * T / (kstat[kn]["median_us"] * 1e-6) / 1e9, 1)}
+                  for kn in DCMHA_KERNELS}
+    dominant = max(DCMHA_PASSES, key=lambda pn: pstat[pn]["median_us"])
+    dom = passes[dominant]
+    pairs = valid_pairs(w.doc, w.window)
+    # MFMA work per admitted pair: forward scores + values 4Hd; backward dR,
+    # scores, dQ, dV, dK 10Hd (the H x H compositions are VALU work)
+    alg_tflops = 14.0 * H * d * pairs / (ms_per_step * 1e-3) / 1e12
+    value = T / (ms_per_step * 1e-3)
+    ceiling_tps = HBM_PEAK_GBPS * 1e9 / sum(spec.values())
+    line = {
+        "metric": DCMHA_METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "heads": H, "head_dim": d, "window": w.window,
+                   "recipe": w.recipe, "valid_pairs": pairs, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "launches": dom["kernels"],
+                     "achieved": dom["alg_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dom["frac"], "traffic": dom["traffic"],
+                     "traffic_over_alg": dom["traffic_over_alg"],
+                     "alg_bytes_per_launch": dom["alg_bytes_per_launch"],
+                     "design_bytes_per_launch": dom["design_bytes_per_launch"]},
+        "mfma_peak_frac": round(alg_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
+        "alg_TFLOPs": round(alg_tflops, 2),
+        "step_hbm_ceiling_tokens_per_s": round(ceiling_tps, 1),
+        "step_roofline_frac": round(value / ceiling_tps, 4),
+        "passes": passes,
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = dcmha_cpu_baseline(w, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def bench_mudd(args):
     import torch
     import dynamic_head_composition_amd as ldc
@@ -325,8 +496,9 @@ def main():
     # (measured: 5 warm-up steps read ~10% below 100); 100 steps take ~50 ms
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = GPT-2 small layer fwd+bwd)")
-    ap.add_argument("--workload", choices=("ldc", "mudd"), default="ldc",
-                    help="ldc: the Lightweight DC layer (default); mudd: MUDD layer mixing")
+    ap.add_argument("--workload", choices=("ldc", "dcmha", "mudd"), default="ldc",
+                    help="ldc: the Lightweight DC layer (default); dcmha: full DCMHA composition at "
+                         "the same shape; mudd: MUDD layer mixing")
     ap.add_argument("--tokens", type=int, default=None, help="truncate the stream (quick runs only)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -342,6 +514,8 @@ def main():
         sys.exit(2)
     if args.workload == "mudd":
         return bench_mudd(args)
+    if args.workload == "dcmha":
+        return bench_dcmha(args)
 
     import torch
     import dynamic_head_composition_amd as ldc

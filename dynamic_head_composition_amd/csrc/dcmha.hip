@@ -28,8 +28,14 @@
 //           for the key side).
 //  * bwd_kv (key-centric): dV_h = R_h^T dO_h and dK_h = scale dS_h^T Q_h from
 //           the bands: token contractions only.
-// Bands use the Lightweight DC band layout, one per head: block (qb, h) at
-// word (qb*H + h) * kBandWords.  Deterministic: no atomics, every output
+// Bands: one 2,048-word block per 16-query block qb and head h, at word
+// (qb*H + h) * kBandWords.  The R and dS bands, read by the key-centric
+// kernel, use the Lightweight DC layout ([key block][key 16][query 16]: a
+// key-centric lane reads its 4 queries as one 16-byte word group).  The P
+// band is read only by query-centric waves and is stored query-major
+// ([key block][query 16][key 16]): lane (g, n) holds keys 4g..4g+3 of block
+// b, one 16-byte piece at word b*256 + n*16 + 4g, so it is written and read
+// as whole 1 KB lines per block.  Deterministic: no atomics, every output
 // element written once.
 #include "dcmha_internal.h"
 #include "ldc_device.hpp"
@@ -201,7 +207,15 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
       const float inv = sum > 0.f ? 1.f / sum : 0.f;
 #pragma unroll
       for (int b = 0; b < kKeyBlocks; ++b) z[h][b] *= inv;
-      if (save && wval) write_band<T, true>(a.pband + ((size_t)qb * H + h) * kBandWords, z[h], xp, g, n);
+      if (save && wval) {  // query-major P band: 16 bytes per lane and key block
+        uint32_t* blk = a.pband + ((size_t)qb * H + h) * kBandWords;
+#pragma unroll
+        for (int b = 0; b < kKeyBlocks; ++b)
+          __builtin_nontemporal_store(
+              u32x4{band_encode<T>(z[h][b][0]), band_encode<T>(z[h][b][1]), band_encode<T>(z[h][b][2]),
+                    band_encode<T>(z[h][b][3])},
+              reinterpret_cast<u32x4*>(blk + b * 256 + n * 16 + 4 * g));
+      }
     }
   });
 
@@ -305,6 +319,18 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
   issue_doc<R, NW>(s_doc, a.doc, span0, a.T);
   RowFrag<T, D> fb[2];
   load_row_frag<T, D>(fb[0], dO + (size_t)tc * H * D, g);
+  // Every head's saved P of this wave's queries (query-major band: one
+  // 16-byte piece per head and key block), in flight during the V phase.
+  u32x4 pw[HM][kKeyBlocks];
+  {
+    const uint32_t* pblk = a.pband + (size_t)(wval ? qb : 0) * H * kBandWords;
+#pragma unroll
+    for (int h = 0; h < HM; ++h)
+#pragma unroll
+      for (int b = 0; b < kKeyBlocks; ++b)
+        pw[h][b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            pblk + (size_t)(h < H ? h : 0) * kBandWords + b * 256 + n * 16 + 4 * g));
+  }
   wait_dma();
 
   uint32_t mbits = 0;
@@ -361,30 +387,41 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
 
   // ---- mixing: dCW = dR P^T, dP = CW^T dR, dZ = P (dP - rowsum(dP P)) ----
   {
+    // P of every head, decoded in place (heads past H hold 0)
+    f32x4 pv[HM][kKeyBlocks];
+#pragma unroll
+    for (int h = 0; h < HM; ++h)
+#pragma unroll
+      for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t u = pw[h][b][i];
+          pv[h][b][i] = h < H ? band_decode<T>(u) : 0.f;
+        }
+    // dCW[t,h,h'] = sum_s dR_h P_h'
+#pragma unroll
+    for (int h = 0; h < HM; ++h)
+#pragma unroll
+      for (int h2 = 0; h2 < HM; ++h2) {
+        float x = 0.f;
+#pragma unroll
+        for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x = fmaf(dr[h][b][i], pv[h2][b][i], x);
+        x = wave_sum4(x);
+        if (tval && g == 0 && h < H && h2 < H) a.dcw[((size_t)t * H + h) * H + h2] = x;
+      }
+    // dP_h' = sum_h CW[t,h,h'] dR_h (in place), and rowsum(dP_h' P_h')
     float cwr[HM][HM];
 #pragma unroll
     for (int h = 0; h < HM; ++h)
 #pragma unroll
       for (int h2 = 0; h2 < HM; ++h2) cwr[h][h2] = (h < H && h2 < H) ? comp_at(a.cw, tc, H, h, h2) : 0.f;
-    const uint32_t* pblk = a.pband + (size_t)(wval ? qb : 0) * H * kBandWords;
-    auto load_p = [&](float (&pv)[HM][4], int b) __attribute__((always_inline)) {
+    float dlt[HM];
 #pragma unroll
-      for (int h = 0; h < HM; ++h)
+    for (int h = 0; h < HM; ++h) dlt[h] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pv[h][i] = h < H ? band_decode<T>(pblk[(size_t)h * kBandWords + b * 256 + (4 * g + i) * 16 + n]) : 0.f;
-    };
-    float dlt[HM], dcw[HM][HM];
-#pragma unroll
-    for (int h = 0; h < HM; ++h) {
-      dlt[h] = 0.f;
-#pragma unroll
-      for (int h2 = 0; h2 < HM; ++h2) dcw[h][h2] = 0.f;
-    }
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      float pv[HM][4];
-      load_p(pv, b);
+    for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float dp[HM];
@@ -396,33 +433,19 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
           dp[h2] = x;
         }
 #pragma unroll
-        for (int h = 0; h < HM; ++h)
-#pragma unroll
-          for (int h2 = 0; h2 < HM; ++h2) dcw[h][h2] = fmaf(dr[h][b][i], pv[h2][i], dcw[h][h2]);
-#pragma unroll
         for (int h2 = 0; h2 < HM; ++h2) {
           dr[h2][b][i] = dp[h2];
-          dlt[h2] = fmaf(dp[h2], pv[h2][i], dlt[h2]);
+          dlt[h2] = fmaf(dp[h2], pv[h2][b][i], dlt[h2]);
         }
       }
-    }
+    // dZ_h = P_h (dP_h - rowsum(dP_h P_h))
 #pragma unroll
     for (int h = 0; h < HM; ++h) {
-      dlt[h] = wave_sum4(dlt[h]);
+      const float dl = wave_sum4(dlt[h]);
 #pragma unroll
-      for (int h2 = 0; h2 < HM; ++h2) {
-        const float x = wave_sum4(dcw[h][h2]);
-        if (tval && g == 0 && h < H && h2 < H) a.dcw[((size_t)t * H + h) * H + h2] = x;
-      }
-    }
+      for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      float pv[HM][4];
-      load_p(pv, b);
-#pragma unroll
-      for (int h = 0; h < HM; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dr[h][b][i] = pv[h][i] * (dr[h][b][i] - dlt[h]);
+        for (int i = 0; i < 4; ++i) dr[h][b][i] = pv[h][b][i] * (dr[h][b][i] - dl);
     }
   }
 
