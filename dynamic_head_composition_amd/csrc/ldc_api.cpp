@@ -22,12 +22,14 @@ bool scale_ok(float scale) { return scale > 0.f && scale < 3.0e38f; }  // positi
 
 int check_common(int dtype, int64_t T, int H, int d, int window) {
   if (dtype != LDC_BF16 && dtype != LDC_F32) return LDC_ERR_DTYPE;
-  if (T < 0 || H < 1 || window < 1 || window > 113) return LDC_ERR_SHAPE;
+  if (T < 0 || H < 1 || window < 1 || window > 128) return LDC_ERR_SHAPE;
   if (d < 1) return LDC_ERR_SHAPE;
   // T*H*d elements must index with 32-bit rows; keep a margin of one tile.
   const int64_t elems = T * (int64_t)H * (int64_t)d;
   if (T > (int64_t)1 << 30 || elems + 512LL * H * d >= ((int64_t)1 << 31)) return LDC_ERR_SHAPE;
   if (!head_dim_supported(dtype, d)) return LDC_ERR_UNSUPPORTED;
+  // float32 rows of 128 leave no LDS for the 10-block band's longer halo
+  if (dtype == LDC_F32 && d == 128 && window > 113) return LDC_ERR_UNSUPPORTED;
   return LDC_OK;
 }
 
@@ -44,7 +46,9 @@ const char* ldc_status_str(int status) {
     case LDC_ERR_SHAPE: return "LDC_ERR_SHAPE: size or window out of range";
     case LDC_ERR_DTYPE: return "LDC_ERR_DTYPE: unknown dtype";
     case LDC_ERR_ALIGN: return "LDC_ERR_ALIGN: pointer not 16-byte aligned";
-    case LDC_ERR_UNSUPPORTED: return "LDC_ERR_UNSUPPORTED: head dim not available for this dtype";
+    case LDC_ERR_UNSUPPORTED:
+      return "LDC_ERR_UNSUPPORTED: head dim (or, for float32 d=128, a window above 113) not available "
+             "for this dtype";
     case LDC_ERR_WORKSPACE: return "LDC_ERR_WORKSPACE: workspace missing or too small";
     case LDC_ERR_HIP: return "LDC_ERR_HIP: a HIP launch failed";
     case LDC_ERR_SCRATCH:
@@ -56,18 +60,18 @@ const char* ldc_status_str(int status) {
 
 size_t ldc_saved_bytes(int dtype, int64_t T, int H, int d, int window) {
   if (check_common(dtype, T, H, d, window) != LDC_OK) return 0;
-  return ldc::saved_band_bytes(T) + (size_t)T * (size_t)H * sizeof(float2);
+  return ldc::saved_band_bytes(T, window) + (size_t)T * (size_t)H * sizeof(float2);
 }
 
 // The backward pass's own scratch (the dPbar band), after room for the saved
 // state it recomputes when the caller passes none (256-byte aligned).
-static size_t bwd_own_bytes(int64_t T) { return ldc::saved_band_bytes(T); }
+static size_t bwd_own_bytes(int64_t T, int window) { return ldc::saved_band_bytes(T, window); }
 static size_t state_room(size_t saved) { return (saved + 255) & ~(size_t)255; }
 
 size_t ldc_bwd_workspace_bytes(int dtype, int64_t T, int H, int d, int window) {
   if (check_common(dtype, T, H, d, window) != LDC_OK) return 0;
   if (T == 0) return 0;
-  return state_room(ldc_saved_bytes(dtype, T, H, d, window)) + bwd_own_bytes(T);
+  return state_room(ldc_saved_bytes(dtype, T, H, d, window)) + bwd_own_bytes(T, window);
 }
 
 int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale, const void* q,
@@ -87,7 +91,7 @@ int ldc_fwd(int dtype, int64_t T, int H, int d, int window, float scale, const v
     if (!aligned16(saved)) return LDC_ERR_ALIGN;
   }
   uint32_t* band = static_cast<uint32_t*>(saved);
-  float2* stats = saved ? reinterpret_cast<float2*>(static_cast<char*>(saved) + ldc::saved_band_bytes(T))
+  float2* stats = saved ? reinterpret_cast<float2*>(static_cast<char*>(saved) + ldc::saved_band_bytes(T, window))
                         : nullptr;
   ldc::FwdArgs a{(int)T, H, window, scale, q, k, v, c, g, doc_ids, o, band, stats};
   hipError_t e = ldc::fwd_dispatch(dtype, d, a, true, static_cast<hipStream_t>(stream));
@@ -117,7 +121,7 @@ static int bwd_validate(int dtype, int64_t T, int H, int d, int window, float sc
     if (!aligned16(saved)) return LDC_ERR_ALIGN;
   }
   // Without saved state the workspace first holds the recomputed state.
-  *need_ws = (saved ? 0 : state_room(need_saved)) + bwd_own_bytes(T);
+  *need_ws = (saved ? 0 : state_room(need_saved)) + bwd_own_bytes(T, window);
   return LDC_OK;
 }
 
@@ -137,13 +141,13 @@ static int bwd_run(int parts, int dtype, int64_t T, int H, int d, int window, fl
       ldc::FwdArgs f{(int)T, H, window, scale, q, k, v, c, g, doc_ids, nullptr,
                      static_cast<uint32_t*>(const_cast<void*>(state)),
                      reinterpret_cast<float2*>(static_cast<char*>(const_cast<void*>(state)) +
-                                               ldc::saved_band_bytes(T))};
+                                               ldc::saved_band_bytes(T, window))};
       if (ldc::fwd_dispatch(dtype, d, f, false, hs) != hipSuccess) return LDC_ERR_HIP;
     }
   }
   const uint32_t* band = static_cast<const uint32_t*>(state);
   const float2* stats =
-      reinterpret_cast<const float2*>(static_cast<const char*>(state) + ldc::saved_band_bytes(T));
+      reinterpret_cast<const float2*>(static_cast<const char*>(state) + ldc::saved_band_bytes(T, window));
   ldc::BwdArgs a{(int)T, H, window, scale, q, k, v, dO, c, g, doc_ids,
                  dq, dk, dv, dc, dg, band, stats, reinterpret_cast<float*>(ws)};
   hipError_t e = ldc::bwd_dispatch(dtype, d, a, parts, hs);

@@ -16,7 +16,7 @@
 //    Phases over the heads: V_h staged (B_h, dPbar, dG); then, with dPbar
 //    complete and written to the workspace band, K_h staged (P_h from the
 //    scores and the saved statistics, dC, dS, dQ).
-//  * bwd_kv (key-centric): each wave owns 16 keys and the 128 queries whose
+//  * bwd_kv (key-centric): each wave owns 16 keys and the 16*NB queries whose
 //    windows can hold them; Pbar and dPbar come from the two bands.  Phases:
 //    dO_h staged (dV_h), then Q_h staged (P_h, dS_h, dK_h).
 // Neither writes a T x window x H map: per-head quantities live in registers
@@ -34,9 +34,11 @@ namespace ldc {
 // bwd_q: per query.  Transposed orientation as in the forward: lane = query
 // column n, 32 band entries (key rows 4g+i of block b) in registers.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int NB>
 __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   constexpr int BQ = 16 * NW;
+  constexpr int kHalo = halo_rows<NB>();
+  constexpr int kBandWords = band_words<NB>();
   constexpr int R = BQ + kHalo;
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
@@ -92,9 +94,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   const size_t bandb = (size_t)(wval ? qb : 0) * kBandWords;  // this wave's band block
   // The shared map saved by the forward pass (masked entries are stored as 0).
   // Each band word is read once here: non-temporal loads (bwd_q -1%).
-  uint32_t bandv[kKeyBlocks][4];
+  uint32_t bandv[NB][4];
 #pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       bandv[b][i] = __builtin_nontemporal_load(a.band + bandb + b * 256 + (4 * g + i) * 16 + n);
@@ -118,32 +120,32 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   preload(dO, a.g, false);
   wait_dma();
 
-  uint32_t mbits = 0;
+  MaskT<NB> mbits = 0;
   {
     const int dt = s_doc[brow + kHalo + n];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = brow + 16 * b + 4 * g + i;
         const int s = span0 + r;
         const bool ok = tval & (s >= 0) & (s <= t) & (t - s < a.window) & (s_doc[r] == dt);
-        mbits |= (ok ? 1u : 0u) << (4 * b + i);
+        mbits |= (MaskT<NB>)(ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  const uint32_t full = full_blocks(mbits);  // wave-uniform
-  f32x4 pb[kKeyBlocks];
+  const uint32_t full = full_blocks<NB>(mbits);  // wave-uniform
+  f32x4 pb[NB];
 #pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) pb[b][i] = band_decode<T>(bandv[b][i]);
 
   // ---- phase 0 (V_h staged): B_h = dO_h V_h^T, dPbar, dG ----
   // Small results are stored at the start of the next stage, after its
   // barrier, so the stage wait (vmcnt 0) never waits for fresh stores.
-  f32x4 dpb[kKeyBlocks];
+  f32x4 dpb[NB];
 #pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) dpb[b] = zero4();
+  for (int b = 0; b < NB; ++b) dpb[b] = zero4();
   float dg_val = 0.f;
   int dg_h = -1;
   auto flush_dg = [&]() {
@@ -168,9 +170,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     const RowFrag<T, D>& df = fb[B];
     const float gh = sb[B];
     float dgs = 0.f;
-    f32x4 bt[kKeyBlocks];
+    f32x4 bt[NB];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
+    for (int b = 0; b < NB; ++b) {
       bt[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, df);
       if (b == 1) issue_part(0, j, bc, Part<1>{});
       if (b == 3) issue_part(0, j, bc, Part<2>{});
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     // contraction (right after the barrier every wave's issue would contend)
     prefetch(j, bc, last ? q : dO, last ? a.c : a.g, last);
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // masked entries of pb are exactly 0; bt there is finite (zero-filled rows)
@@ -196,15 +198,15 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     // dPbar of this wave's block, for the key-centric kernel
     uint32_t* blk = reinterpret_cast<uint32_t*>(a.dband) + bandb;
     if constexpr (Elem<T>::bf16) {
-      uint32_t wv[kKeyBlocks][4];
+      uint32_t wv[NB][4];
 #pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) wv[b][i] = __float_as_uint(dpb[b][i]);
       store_band_block(blk, wv, s_xp + w * 512, g, n);
     } else {
 #pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) blk[b * 256 + (4 * g + i) * 16 + n] = __float_as_uint(dpb[b][i]);
     }
@@ -247,9 +249,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     const float ch = sb[B];
     const float2 st = stb[B];  // (row max in log2 units, 1/row sum) saved by the forward pass
     // e = exp2(s*scale*log2e - max) = P_h / inv; masked entries 0
-    f32x4 p[kKeyBlocks];
+    f32x4 p[NB];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
+    for (int b = 0; b < NB; ++b) {
       p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf);
       if (b == 1) issue_part(1, j, bc, Part<1>{});
       if (b == 3) issue_part(1, j, bc, Part<2>{});
@@ -257,26 +259,26 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
     }
     prefetch(j, bc, q, a.c, true);  // next stage's operands (see the V phase)
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[b][i] = exp2_scaled(p[b][i], sl2, st.x);  // as in the forward pass
     mask_band(p, mbits, full, 0.f);
     float dcs = 0.f;
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dcs = fmaf(p[b][i], dpb[b][i], dcs);
     dcs = wave_sum4(dcs) * st.y;  // dC = sum_s P_h dPbar
     dc_val = dcs;
     const float cs = ch * st.y;   // dS = C P (dPbar - dC) = (C inv) e (dPbar - dC)
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[b][i] = cs * p[b][i] * (dpb[b][i] - dcs);
-    BandOperand<T> dso;
+    BandOperand<T, NB> dso;
     dso.set(p);
     __builtin_amdgcn_s_setprio(0);
-    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, prev);
+    mma_tcontract<T, D, NB>(pend, cur, brow, lo, dso, g, n, prev);
     pend_h = j;
   });
   flush_dq();
@@ -285,13 +287,15 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // bwd_kv: per key.  Normal orientation S = Q K^T: lane = key column n, rows
-// 4g+i of query block b in registers; the wave's queries are the 128 tokens
-// [kw, kw+128) that can hold its keys in their windows.
+// 4g+i of query block b in registers; the wave's queries are the 16*NB tokens
+// [kw, kw+16*NB) that can hold its keys in their windows.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int NB>
 __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   constexpr int BK = 16 * NW;
-  constexpr int R = BK + kHalo;  // query rows [k0, k0 + BK + 112)
+  constexpr int kHalo = halo_rows<NB>();
+  constexpr int kBandWords = band_words<NB>();
+  constexpr int R = BK + kHalo;  // query rows [k0, k0 + BK + kHalo)
   constexpr int RP = (R + 63) / 64 * 64;
   // per-row scalars of the staged head: C, G, dC, row max, 1/row sum
   enum { SC_C = 0, SC_G = 1, SC_DC = 2, SC_MX = 3, SC_INV = 4, NSC = 5 };
@@ -361,39 +365,39 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   issue(0, 0, true, Buf<0>{});
   issue_doc<R, NW>(s_doc, a.doc, span0, a.T);
   // Pbar (phase 0) and dPbar (phase 1) of this lane's (key, 4 queries)
-  // entries, from the bands: query block kq + b, key block 7 - b, 16 bytes
+  // entries, from the bands: query block kq + b, key block NB-1-b, 16 bytes
   // per block; entries beyond the stream or outside the window read as 0.
   // Loaded non-temporally, like every band read (bwd_kv -3%).
   const int kq = (k0 >> 4) + w;
   const int nqb = (a.T + 15) >> 4;
   auto band_word = [&](int b) {
     const int qbk = kq + b < nqb ? kq + b : nqb - 1;
-    return (size_t)qbk * kBandWords + (7 - b) * 256 + n * 16 + 4 * g;
+    return (size_t)qbk * kBandWords + (NB - 1 - b) * 256 + n * 16 + 4 * g;
   };
-  uint4 bandv[kKeyBlocks];
+  uint4 bandv[NB];
 #pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b)
+  for (int b = 0; b < NB; ++b)
     bandv[b] = __builtin_bit_cast(
         uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.band + band_word(b))));
   wait_dma();
 
-  uint32_t mbits = 0;  // bit 4b+i <-> query row brow + 16b + 4g + i
+  MaskT<NB> mbits = 0;  // bit 4b+i <-> query row brow + 16b + 4g + i
   {
     const int ds = s_doc[brow + n];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = brow + 16 * b + 4 * g + i;
         const int t = span0 + r;
         const bool ok = sval & (t < a.T) & (t >= s) & (t - s < a.window) & (s_doc[r] == ds);
-        mbits |= (ok ? 1u : 0u) << (4 * b + i);
+        mbits |= (MaskT<NB>)(ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  const uint32_t full = full_blocks(mbits);  // wave-uniform
-  f32x4 pb[kKeyBlocks];
+  const uint32_t full = full_blocks<NB>(mbits);  // wave-uniform
+  f32x4 pb[NB];
 #pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) {
+  for (int b = 0; b < NB; ++b) {
     const uint32_t uu[4] = {bandv[b].x, bandv[b].y, bandv[b].z, bandv[b].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) pb[b][i] = keep_admitted(mbits, b, i, band_decode<T>(uu[i]), 0.f);
@@ -419,11 +423,11 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
 
   // Q phase operands loaded during the last dO stage: dPbar of this lane's
   // (key, 4 queries) entries and the first head's K fragment.
-  f32x4 dpb[kKeyBlocks];
+  f32x4 dpb[NB];
   RowFrag<T, D> kfb[2];
   auto load_q_phase = [&]() {
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
+    for (int b = 0; b < NB; ++b) {
       const f32x4 d4 =
           __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.dband + band_word(b)));
       dpb[b] = d4;  // only multiplied by P_h, which is 0 where masked
@@ -446,16 +450,16 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
       flush(a.dv, 1.f);
       return;
     }
-    f32x4 gp[kKeyBlocks];
+    f32x4 gp[NB];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
+    for (int b = 0; b < NB; ++b) {
       const float4 g4 = rows4(sc, SC_G, b);
       gp[b] = f32x4{g4.x * pb[b][0], g4.y * pb[b][1], g4.z * pb[b][2], g4.w * pb[b][3]};
     }
-    BandOperand<T> op;
+    BandOperand<T, NB> op;
     op.set(gp);
     __builtin_amdgcn_s_setprio(1);
-    mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n, pending(a.dv, 1.f), [&](auto pp) {
+    mma_tcontract<T, D, NB>(pend, cur, brow, lo, op, g, n, pending(a.dv, 1.f), [&](auto pp) {
       if constexpr (decltype(pp)::value < kIssueParts) issue_part(0, j, bc, pp);
     });
     issue_rest(0, j, bc, Part<tcontract_groups<T, D>()>{});
@@ -484,9 +488,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
       return;
     }
     const RowFrag<T, D>& kf = kfb[B];
-    f32x4 p[kKeyBlocks];
+    f32x4 p[NB];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
+    for (int b = 0; b < NB; ++b) {
       p[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, kf);
       if (b == 1) issue_part(1, j, bc, Part<1>{});
       if (b == 3) issue_part(1, j, bc, Part<2>{});
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
     // next head's K row, issued after this stage's DMA and score contraction
     load_row_frag<T, D>(kfb[1 - B], k + ((size_t)sc_ * H + (j + 1 < H ? j + 1 : 0)) * D, g);
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
+    for (int b = 0; b < NB; ++b) {
       const float4 mx = rows4(sc, SC_MX, b), inv = rows4(sc, SC_INV, b);
       const float4 c4 = rows4(sc, SC_C, b), dc4 = rows4(sc, SC_DC, b);
       const float mxv[4] = {mx.x, mx.y, mx.z, mx.w}, invv[4] = {inv.x, inv.y, inv.z, inv.w};
@@ -506,40 +510,43 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
         p[b][i] = (cv[i] * invv[i]) * exp2_scaled(p[b][i], sl2, mxv[i]) * (dpb[b][i] - dcv[i]);
     }
     mask_band(p, mbits, full, 0.f);
-    BandOperand<T> dso;
+    BandOperand<T, NB> dso;
     dso.set(p);
     __builtin_amdgcn_s_setprio(0);
-    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, prev);
+    mma_tcontract<T, D, NB>(pend, cur, brow, lo, dso, g, n, prev);
     pend_h = j;
   });
   flush(a.dk, a.scale);
   wait_dma();
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int NB>
 static hipError_t launch_bwd(const BwdArgs& a, int parts, hipStream_t st) {
   constexpr int B = 16 * NW;
   const int nblk = (int)((a.T + B - 1) / B);
   if (parts & 1) {
-    hipLaunchKernelGGL((bwd_q_kernel<T, D, NW>), dim3(nblk), dim3(NW * kWave), 0, st, a);
+    hipLaunchKernelGGL((bwd_q_kernel<T, D, NW, NB>), dim3(nblk), dim3(NW * kWave), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (parts & 2) {
-    hipLaunchKernelGGL((bwd_kv_kernel<T, D, NW>), dim3(nblk), dim3(NW * kWave), 0, st, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, NW, NB>), dim3(nblk), dim3(NW * kWave), 0, st, a);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
+// Windows up to 113 keys: 8-block bands; wider (up to 128): 10-block bands in
+// 4-wave workgroups (one wave per SIMD, up to 512 registers).
 hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, int parts, hipStream_t st) {
+  const bool wide = a.window > kMaxWindow;
   if (dtype == 0) {
-    if (d == 128) return launch_bwd<bf16_t, 128, 8>(a, parts, st);
-    if (d == 64) return launch_bwd<bf16_t, 64, 8>(a, parts, st);
+    if (d == 128) return wide ? launch_bwd<bf16_t, 128, 4, 10>(a, parts, st) : launch_bwd<bf16_t, 128, 8, 8>(a, parts, st);
+    if (d == 64) return wide ? launch_bwd<bf16_t, 64, 4, 10>(a, parts, st) : launch_bwd<bf16_t, 64, 8, 8>(a, parts, st);
   } else {
-    if (d == 128) return launch_bwd<float, 128, 2>(a, parts, st);
-    if (d == 64) return launch_bwd<float, 64, 4>(a, parts, st);
-    if (d == 16) return launch_bwd<float, 16, 4>(a, parts, st);
+    if (d == 128 && !wide) return launch_bwd<float, 128, 2, 8>(a, parts, st);
+    if (d == 64) return wide ? launch_bwd<float, 64, 4, 10>(a, parts, st) : launch_bwd<float, 64, 4, 8>(a, parts, st);
+    if (d == 16) return wide ? launch_bwd<float, 16, 4, 10>(a, parts, st) : launch_bwd<float, 16, 4, 8>(a, parts, st);
   }
   return hipErrorInvalidValue;
 }

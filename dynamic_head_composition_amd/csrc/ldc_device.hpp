@@ -50,6 +50,21 @@ constexpr int kHalo = kBand - 16;             // 112 rows before a 16-row block
 constexpr int kMaxWindow = kHalo + 1;         // 113: widest window the band holds
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Bands of NB key blocks (NB even: the bf16 token contraction takes key
+// blocks in pairs).  NB = 8 holds windows up to 113 keys; NB = 10 up to 145
+// (the widest window accepted is 128).  A lane holds 4 entries per block:
+// its admission bits fit 32 bits for NB <= 8, 64 bits beyond.
+template <int NB>
+constexpr int halo_rows() {
+  return 16 * (NB - 1);
+}
+template <int NB>
+constexpr int band_words() {
+  return NB * 256;
+}
+template <int NB>
+using MaskT = typename std::conditional<(NB * 4 <= 32), uint32_t, uint64_t>::type;
+
 // f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -154,13 +169,14 @@ __device__ __forceinline__ float swap32_sum(float x) {
 __device__ __forceinline__ float wave_max4(float x) { return swap32_max(swap16_max(x)); }
 __device__ __forceinline__ float wave_sum4(float x) { return swap32_sum(swap16_sum(x)); }
 
-// Wave-uniform bit mask over the 8 token blocks of a wave's band, from the
-// lane's 32 admission bits (bit 4b+i): bit b set when every entry of block b
+// Wave-uniform bit mask over the NB token blocks of a wave's band, from the
+// lane's admission bits (bit 4b+i): bit b set when every entry of block b
 // of every lane is admitted (no per-entry masking needed there).
-__device__ __forceinline__ uint32_t full_blocks(uint32_t mbits) {
+template <int NB = kKeyBlocks>
+__device__ __forceinline__ uint32_t full_blocks(MaskT<NB> mbits) {
   uint32_t full = 0;
 #pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b)
+  for (int b = 0; b < NB; ++b)
     full |= (__all(((mbits >> (4 * b)) & 15u) == 15u) ? 1u : 0u) << b;
   // one packed scalar, opaque, rather than 8 lane masks kept live for the tests
   asm volatile("" : "+s"(full));
@@ -173,10 +189,18 @@ __device__ __forceinline__ float keep_admitted(uint32_t mbits, int b, int i, flo
   const int m = (int)(mbits << (31 - (4 * b + i))) >> 31;  // all ones when admitted
   return __int_as_float((__float_as_int(x) & m) | (__float_as_int(other) & ~m));
 }
+__device__ __forceinline__ float keep_admitted(uint64_t mbits, int b, int i, float x, float other) {
+  const int m = (int)((int64_t)(mbits << (63 - (4 * b + i))) >> 63);
+  return __int_as_float((__float_as_int(x) & m) | (__float_as_int(other) & ~m));
+}
 // The value unchanged, but opaque to the optimizer: used once per stage on
 // the admission bits so that the 32 per-entry masks are formed where they are
 // used instead of being hoisted out of the stage loop and kept live.
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ uint64_t opaque(uint64_t x) {
   asm volatile("" : "+v"(x));
   return x;
 }
@@ -191,19 +215,20 @@ __device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
 // In a wave whose band lies inside one document, only the first and the last
 // token blocks are partial (the window's far edge and the causal diagonal);
 // that case takes a branch of its own, the general case tests every block.
-__device__ __forceinline__ void mask_band(f32x4 (&p)[kKeyBlocks], uint32_t mbits, uint32_t full,
-                                          float other) {
-  constexpr uint32_t kInner = ((1u << kKeyBlocks) - 1) & ~1u & ~(1u << (kKeyBlocks - 1));
-  const uint32_t mb = opaque(mbits), fl = opaque_s(full);
+template <int NB = kKeyBlocks>
+__device__ __forceinline__ void mask_band(f32x4 (&p)[NB], MaskT<NB> mbits, uint32_t full, float other) {
+  constexpr uint32_t kInner = ((1u << NB) - 1) & ~1u & ~(1u << (NB - 1));
+  const MaskT<NB> mb = opaque(mbits);
+  const uint32_t fl = opaque_s(full);
   if (fl == kInner) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p[0][i] = keep_admitted(mb, 0, i, p[0][i], other);
-      p[kKeyBlocks - 1][i] = keep_admitted(mb, kKeyBlocks - 1, i, p[kKeyBlocks - 1][i], other);
+      p[NB - 1][i] = keep_admitted(mb, NB - 1, i, p[NB - 1][i], other);
     }
   } else {
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
       if (!((fl >> b) & 1u))
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[b][i] = keep_admitted(mb, b, i, p[b][i], other);
@@ -385,20 +410,20 @@ __device__ __forceinline__ f32x4 mma_dcontract(f32x4 acc, const T* tile, int row
   return acc;
 }
 
-// Token-contraction operand: a 16 x 128 band held in accumulator layout
+// Token-contraction operand: a 16 x 16NB band held in accumulator layout
 // (lane: token rows 4g+i of block b, column n) packed as B-operand k-chunks.
 // bf16: chunk ks covers blocks 2ks, 2ks+1; slot j <-> block 2ks + j/4, row 4g + j%4.
 // The fp32 band is carried as two bf16 operands, hi = bf16(x) and
 // lo = bf16(x - hi), so the contraction keeps ~16 mantissa bits of x; the
 // other operand (a bf16 input tensor) is exact.
-template <typename T>
+template <typename T, int NB = kKeyBlocks>
 struct BandOperand;
-template <>
-struct BandOperand<bf16_t> {
-  bf16x8 hi[kKeyBlocks / 2], lo[kKeyBlocks / 2];
-  __device__ __forceinline__ void set(const f32x4 (&p)[kKeyBlocks]) {
+template <int NB>
+struct BandOperand<bf16_t, NB> {
+  bf16x8 hi[NB / 2], lo[NB / 2];
+  __device__ __forceinline__ void set(const f32x4 (&p)[NB]) {
 #pragma unroll
-    for (int ks = 0; ks < kKeyBlocks / 2; ++ks) {
+    for (int ks = 0; ks < NB / 2; ++ks) {
       u32x4 h4, l4;
 #pragma unroll
       for (int jp = 0; jp < 4; ++jp) {
@@ -417,12 +442,12 @@ struct BandOperand<bf16_t> {
     }
   }
 };
-template <>
-struct BandOperand<float> {
-  f32x4 v[kKeyBlocks];
-  __device__ __forceinline__ void set(const f32x4 (&p)[kKeyBlocks]) {
+template <int NB>
+struct BandOperand<float, NB> {
+  f32x4 v[NB];
+  __device__ __forceinline__ void set(const f32x4 (&p)[NB]) {
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) v[b] = p[b];
+    for (int b = 0; b < NB; ++b) v[b] = p[b];
   }
 };
 
@@ -510,7 +535,7 @@ __device__ __forceinline__ void store_row(const PendingRow& pr, const f32x4 (&ac
 // scheduler; every other kind of instruction may still move across it.
 __device__ __forceinline__ void store_fence() { __builtin_amdgcn_sched_barrier(0x00A1); }
 
-// Contraction over the 128 band tokens:  out[d, n] = sum_tok X[tok, d] * P[tok, n]
+// Contraction over the 16NB band tokens:  out[d, n] = sum_tok X[tok, d] * P[tok, n]
 // with X a staged tile (rows base_row + tok) and P the band operand.
 // Result layout (lane: column n; register r = 4*blk + i):
 //   bf16: acc[2p+e][i] <-> d = 32p + 8g + 4(e ^ g%2) + i  (8 consecutive d per p, g)
@@ -535,9 +560,9 @@ struct NoHook {
   template <typename P>
   __device__ __forceinline__ void operator()(P) const {}
 };
-template <typename T, int D, typename Hook = NoHook>
+template <typename T, int D, int NB = kKeyBlocks, typename Hook = NoHook>
 __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* tile, int row16,
-                                              const LaneOffsets<T, D>& lo, const BandOperand<T>& P,
+                                              const LaneOffsets<T, D>& lo, const BandOperand<T, NB>& P,
                                               int g, int n, const PendingRow& prev,
                                               Hook&& hook = Hook{}) {
   using TL = Tile<T, D>;
@@ -556,7 +581,7 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
 #pragma unroll
       for (int r = 2 * p0; r < 2 * (p0 + PG); ++r) acc[r] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < kKeyBlocks / 2; ++ks) {
+      for (int ks = 0; ks < NB / 2; ++ks) {
 #pragma unroll
         for (int p = p0; p < p0 + PG; ++p) {
 #pragma unroll
@@ -585,7 +610,7 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
 #pragma unroll
     for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
+    for (int b = 0; b < NB; ++b) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * b + 4 * g + i;  // relative to row16
@@ -602,8 +627,8 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
 // ---------------------------------------------------------------------------
 // Saved shared-map band and dPbar band
 // ---------------------------------------------------------------------------
-// Per 16-query block qb: 8 key blocks kb, each a [key 16][query 16] array of
-// 4-byte words; key block kb of query block qb holds keys 16*qb - 112 + 16*kb
+// Per 16-query block qb: NB key blocks kb, each a [key 16][query 16] array of
+// 4-byte words; key block kb of query block qb holds keys 16*qb - 16(NB-1) + 16*kb
 // + (0..15).  Word of the shared map: bf16 path (hi | lo << 16) with
 // hi = bf16(x), lo = bf16(x - hi); fp32 path: the float.  The dPbar band
 // (float32) uses the same indexing.  Query-centric waves (lane = query n,
@@ -641,12 +666,13 @@ __device__ __forceinline__ float band_decode(uint32_t u) {
 // instead of 32 scattered 4-byte accesses per lane.  `blk` is the block's
 // first word (16-byte aligned); one wave's scratch accesses follow each other
 // in LDS order, so no barrier is needed.
-__device__ __forceinline__ void store_band_block(uint32_t* blk, const uint32_t (&wv)[kKeyBlocks][4],
-                                                 float* xp, int g, int n) {
+template <int NB = kKeyBlocks>
+__device__ __forceinline__ void store_band_block(uint32_t* blk, const uint32_t (&wv)[NB][4], float* xp,
+                                                 int g, int n) {
   uint32_t* xs = reinterpret_cast<uint32_t*>(xp);
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int r = 0; r < kKeyBlocks / 2; ++r) {
+  for (int r = 0; r < NB / 2; ++r) {
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll

@@ -32,10 +32,12 @@ namespace ldc {
 // VAL = false: the score phase only, writing the saved state (shared-map band
 // and softmax statistics) and no O: the backward pass's recomputation when the
 // caller kept no saved state.
-template <typename T, int D, int NW, bool VAL = true>
-__global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) void fwd_kernel(
+// NB: key blocks per band (8 for windows up to 113 keys, 10 up to 128).
+template <typename T, int D, int NW, int NB, bool VAL = true>
+__global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16 && NB == 8) ? 4 : 1) void fwd_kernel(
     const FwdArgs a) {
   constexpr int BQ = 16 * NW;
+  constexpr int kHalo = halo_rows<NB>();
   constexpr int R = BQ + kHalo;
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int q0 = tile * BQ;
   const int span0 = q0 - kHalo;  // token of LDS row 0
-  const int brow = 16 * w;       // LDS row of this wave's band start (token qw - 112)
+  const int brow = 16 * w;       // LDS row of this wave's band start (token qw - kHalo)
   const int t = q0 + 16 * w + n; // this lane's query
   const bool tval = t < a.T;
   const int tc = tval ? t : a.T - 1;  // a valid row for unconditional loads
@@ -84,26 +86,26 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
   chb[0] = a.c[(size_t)tc * H];
   wait_dma();
 
-  // Admission mask of this lane's 32 band entries: bit 4b+i <-> key row brow+16b+4g+i.
-  uint32_t mbits = 0;
+  // Admission mask of this lane's 4NB band entries: bit 4b+i <-> key row brow+16b+4g+i.
+  MaskT<NB> mbits = 0;
   {
     const int dt = s_doc[brow + kHalo + n];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = brow + 16 * b + 4 * g + i;
         const int s = span0 + r;
         const bool ok = tval & (s >= 0) & (s <= t) & (t - s < a.window) & (s_doc[r] == dt);
-        mbits |= (ok ? 1u : 0u) << (4 * b + i);
+        mbits |= (MaskT<NB>)(ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  const uint32_t full = full_blocks(mbits);  // wave-uniform
+  const uint32_t full = full_blocks<NB>(mbits);  // wave-uniform
 
   const float sl2 = a.scale * kLog2e;
-  f32x4 pb[kKeyBlocks];
+  f32x4 pb[NB];
 #pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) pb[b] = zero4();
+  for (int b = 0; b < NB; ++b) pb[b] = zero4();
 
   // Softmax statistics of each head go to the saved state for the backward
   // pass; the store is deferred past the next stage's barrier.
@@ -132,9 +134,9 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
     const float ch = chb[B];
     flush_stats();
 
-    f32x4 sc[kKeyBlocks];
+    f32x4 sc[NB];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) sc[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf);
+    for (int b = 0; b < NB; ++b) sc[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf);
     // Raw scores; entries outside the window or document become -inf (only
     // in blocks not fully admitted), so max and exp need no further masking.
     // The scale is positive, so rounding(s * scale*log2e) is monotonic in s
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
     mask_band(sc, mbits, full, -INFINITY);
     float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
     __builtin_amdgcn_s_setprio(0);
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
     const float mxs = mx == -INFINITY ? 0.f : mx * sl2;  // a row with no key: all terms 0
     float sum = 0.f;
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e = exp2_scaled(sc[b][i], sl2, mxs);
@@ -165,27 +167,27 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
     st_inv = inv;
     st_h = j;
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[b][i] += coef * sc[b][i];
   });
 
   flush_stats();
-  BandOperand<T> pop;
+  BandOperand<T, NB> pop;
   pop.set(pb);
   if (a.band && q0 + 16 * w < a.T) {
-    // the wave's 16 x 128 shared map, for the backward pass
-    uint32_t* blk = a.band + (size_t)((q0 >> 4) + w) * kBandWords;
+    // the wave's 16 x 16NB shared map, for the backward pass
+    uint32_t* blk = a.band + (size_t)((q0 >> 4) + w) * band_words<NB>();
     if constexpr (Elem<T>::bf16) {
-      uint32_t wv[kKeyBlocks][4];
+      uint32_t wv[NB][4];
 #pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) wv[b][i] = band_encode<T>(pb[b][i]);
       store_band_block(blk, wv, s_xp + w * 512, g, n);
     } else {
 #pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) blk[b * 256 + (4 * g + i) * 16 + n] = band_encode<T>(pb[b][i]);
     }
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
       return;
     }
     const float gh = ghb[B];
-    mma_tcontract<T, D>(pend, cur, brow, lo, pop, g, n, pending());
+    mma_tcontract<T, D, NB>(pend, cur, brow, lo, pop, g, n, pending());
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int r = 0; r < D / 16; ++r) pend[r] *= gh;
@@ -235,25 +237,29 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16) ? 4 : 1) voi
   wait_dma();  // no DMA may land in LDS after the workgroup ends
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int NB>
 static hipError_t launch_fwd(const FwdArgs& a, bool value, hipStream_t st) {
   constexpr int BQ = 16 * NW;
   const int nblk = (int)((a.T + BQ - 1) / BQ);
   if (value)
-    hipLaunchKernelGGL((fwd_kernel<T, D, NW, true>), dim3(nblk), dim3(NW * kWave), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, NB, true>), dim3(nblk), dim3(NW * kWave), 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, NW, false>), dim3(nblk), dim3(NW * kWave), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, NB, false>), dim3(nblk), dim3(NW * kWave), 0, st, a);
   return hipGetLastError();
 }
 
+// Windows up to 113 keys: 8-block bands.  Wider windows (up to 128): 10-block
+// bands in 4-wave workgroups, one wave per SIMD (the larger band arrays need
+// more than 256 registers; the longer halo needs the LDS of the 8-wave tiles).
 hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, bool value, hipStream_t st) {
+  const bool wide = a.window > kMaxWindow;
   if (dtype == 0) {
-    if (d == 128) return launch_fwd<bf16_t, 128, 8>(a, value, st);
-    if (d == 64) return launch_fwd<bf16_t, 64, 8>(a, value, st);
+    if (d == 128) return wide ? launch_fwd<bf16_t, 128, 4, 10>(a, value, st) : launch_fwd<bf16_t, 128, 8, 8>(a, value, st);
+    if (d == 64) return wide ? launch_fwd<bf16_t, 64, 4, 10>(a, value, st) : launch_fwd<bf16_t, 64, 8, 8>(a, value, st);
   } else {
-    if (d == 128) return launch_fwd<float, 128, 2>(a, value, st);
-    if (d == 64) return launch_fwd<float, 64, 4>(a, value, st);
-    if (d == 16) return launch_fwd<float, 16, 4>(a, value, st);
+    if (d == 128 && !wide) return launch_fwd<float, 128, 2, 8>(a, value, st);
+    if (d == 64) return wide ? launch_fwd<float, 64, 4, 10>(a, value, st) : launch_fwd<float, 64, 4, 8>(a, value, st);
+    if (d == 16) return wide ? launch_fwd<float, 16, 4, 10>(a, value, st) : launch_fwd<float, 16, 4, 8>(a, value, st);
   }
   return hipErrorInvalidValue;
 }

@@ -6,7 +6,8 @@
 
 namespace ldc {
 
-constexpr size_t kBandWordsHost = 8 * 256;  // words per 16-query block
+// Key blocks per band: 8 for windows up to 113 keys, 10 up to 128.
+inline int band_key_blocks(int window) { return window > 113 ? 10 : 8; }
 
 struct FwdArgs {
   int T, H, window;
@@ -31,9 +32,12 @@ struct BwdArgs {
   float* dband;          // workspace: dPbar band, written by bwd_q, read by bwd_kv
 };
 
-// Sizes of the saved state and of the backward workspace.
+// Sizes of the saved state and of the backward workspace: one band block of
+// 256 words per key block and 16-query block.
 inline size_t band_blocks(int64_t T) { return (size_t)((T + 15) / 16); }
-inline size_t saved_band_bytes(int64_t T) { return band_blocks(T) * kBandWordsHost * 4; }
+inline size_t saved_band_bytes(int64_t T, int window) {
+  return band_blocks(T) * (size_t)band_key_blocks(window) * 256 * 4;
+}
 
 // value = false: only the saved state (band and statistics), no O.
 hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, bool value, hipStream_t st);

@@ -25,8 +25,9 @@
  *   doc_ids                    : [T] int32, any values (only equality matters).
  * Pointers are DEVICE pointers owned by the caller; base addresses must be
  * 16-byte aligned.  Supported shapes: d in {64, 128} for LDC_BF16 and
- * d in {16, 64, 128} for LDC_F32; 1 <= window <= 113; H >= 1; T >= 0
- * (T == 0 is a no-op); T*H*d < 2^31.
+ * d in {16, 64, 128} for LDC_F32; 1 <= window <= 128 (LDC_F32 with d = 128:
+ * up to 113, else LDC_ERR_UNSUPPORTED); H >= 1; T >= 0 (T == 0 is a no-op);
+ * T*H*d < 2^31.
  *
  * Execution: work is enqueued on `stream` (a hipStream_t; NULL = the default
  * stream) and the call returns without synchronising.  The library allocates
@@ -55,7 +56,7 @@ typedef enum {
   LDC_ERR_SHAPE = 2,       /* T<0, H<1, window or scale out of range, overflow */
   LDC_ERR_DTYPE = 3,       /* dtype is not an ldc_dtype value               */
   LDC_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned              */
-  LDC_ERR_UNSUPPORTED = 5, /* head dim not instantiated for this dtype      */
+  LDC_ERR_UNSUPPORTED = 5, /* head dim (or window) not available for dtype  */
   LDC_ERR_WORKSPACE = 6,   /* saved state / workspace missing or too small  */
   LDC_ERR_HIP = 7,         /* a HIP launch failed                           */
   LDC_ERR_SCRATCH = 8      /* ldc_bwd_noalloc: problem exceeds its scratch  */
@@ -72,8 +73,9 @@ typedef enum {
  *   textbook choice); other values return LDC_ERR_SHAPE.
  * saved: NULL (inference: nothing saved) or a device buffer of at least
  *   ldc_saved_bytes(...) bytes (16-byte aligned) that receives the state
- *   ldc_bwd needs: the shared map Pbar over each 16-query block's 128-key
- *   band (2,048 words per block; bf16 path: bf16 hi and lo parts) followed by
+ *   ldc_bwd needs: the shared map Pbar over each 16-query block's key band
+ *   (NB blocks of 16 keys, NB = 8 for windows up to 113 and 10 above: NB*256
+ *   words per 16-query block; bf16 path: bf16 hi and lo parts) followed by
  *   each head's softmax statistics [T,H] (row max in log2 units, 1/row sum).
  * O is float32 for both storage dtypes: a bf16 store alone would round
  * outputs of magnitude above ~5 by more than 2e-2. */

@@ -55,6 +55,13 @@ def test_workspace_and_saved_bytes():
     assert ldc.saved_bytes(ldc.LDC_F32, 17, 2, 16, 112) == 2 * 2048 * 4 + 17 * 2 * 8
     assert ldc.workspace_bytes(ldc.LDC_BF16, 0, 6, 128, 112) == 0
     assert ldc.workspace_bytes(ldc.LDC_BF16, 10, 6, 16, 112) == 0  # unsupported -> 0
+    # windows above 113 keys: bands of 10 key blocks (2,560 words per 16-query block)
+    wide = 4096 * 2560 * 4
+    assert ldc.saved_bytes(ldc.LDC_BF16, 65536, 6, 128, 128) == wide + 65536 * 6 * 8
+    assert ldc.saved_bytes(ldc.LDC_BF16, 65536, 6, 128, 114) == wide + 65536 * 6 * 8
+    assert ldc.saved_bytes(ldc.LDC_BF16, 65536, 6, 128, 113) == band + 65536 * 6 * 8
+    assert ldc.workspace_bytes(ldc.LDC_F32, 17, 3, 64, 120) == room(2 * 10240 + 17 * 3 * 8) + 2 * 10240
+    assert ldc.saved_bytes(ldc.LDC_F32, 17, 3, 128, 120) == 0       # f32 d=128: window <= 113
 
 
 def fwd_call(dtype=ldc.LDC_BF16, T=256, H=6, d=128, window=112, ptrs=None, saved=None, saved_bytes=0,
@@ -99,7 +106,8 @@ def test_validation_errors(call):
     assert call(T=-1) == 2                         # LDC_ERR_SHAPE
     assert call(H=0) == 2
     assert call(window=0) == 2
-    assert call(window=114) == 2
+    assert call(window=129) == 2
+    assert call(dtype=ldc.LDC_F32, d=128, window=114) == 5  # no LDS for f32 rows of 128 there
     assert call(T=1 << 31) == 2                    # too many rows
     assert call(scale=0.0) == 2                    # scale must be positive and finite
     assert call(scale=-0.5) == 2

@@ -322,3 +322,36 @@ def test_side_stream(ldc):
     assert torch.equal(o, ref["o"])
     for name, gr in zip(GRADS, grads):
         assert torch.equal(gr, ref[name]), name
+
+
+WIDE = [  # windows of 114..128 keys (10-block bands): (T, H, d, dtype, window, docs, seed)
+    (1, 1, 16, "f32", 128, ("single",), 40),
+    (300, 2, 16, "f32", 128, ("geometric", 90), 41),
+    (257, 3, 64, "f32", 114, ("uniform", 8, 200), 42),
+    (500, 6, 128, "bf16", 128, ("geometric", 300), 43),
+    (1000, 12, 64, "bf16", 120, ("single",), 44),
+    (129, 1, 128, "bf16", 127, ("single",), 45),
+    (700, 5, 64, "bf16", 116, ("geometric", 150), 46),
+    (4096, 6, 128, "bf16", 128, ("geometric", 1024), 47),
+]
+
+
+@pytest.mark.parametrize("T,H,d,dtype,window,docs,seed", WIDE)
+def test_wide_windows(ldc, T, H, d, dtype, window, docs, seed):
+    w = wl.make_workload(T, H, d, dtype=dtype, window=window, docs=docs, seed=seed)
+    check_all(ldc, w)
+
+
+def test_wide_window_without_saved_state(ldc):
+    """Window 128: the backward's own recomputation of the saved state gives
+    bitwise the gradients of the saved one."""
+    import torch
+    w = wl.make_workload(2500, 6, 128, dtype="bf16", window=128, seed=48)
+    x = w.torch_inputs("cuda", with_do=True)
+    args = (x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"])
+    _, saved = ldc.fwd(*args, window=128, scale=w.scale, save=True)
+    a = ldc.bwd(*args, saved, x["do"], window=128, scale=w.scale)
+    b = ldc.bwd(*args, None, x["do"], window=128, scale=w.scale)
+    torch.cuda.synchronize()
+    for name, a_, b_ in zip(GRADS, a, b):
+        assert torch.equal(a_, b_), name
