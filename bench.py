@@ -29,6 +29,9 @@ With --workload dcmha the step is the full DCMHA composition layer (score and
 weight compositions across heads, dcmha_fwd + dcmha_bwd_q + dcmha_bwd_kv) at
 the same GPT-2 small shape, reported in the same format.
 
+With --workload cg the step is the generator of the layer's weights (C = x WC,
+G = x WG from the 768-wide hidden state) forward and backward.
+
 With --workload mudd the step is one MUDD mix forward and backward
 (mudd_fwd + mudd_bwd) over a GPT-2 small token stream (65,536 tokens, model
 dim 768, 13 layer streams, 4 ways), reported in the same format.
@@ -400,6 +403,108 @@ def bench_dcmha(args):
     print(json.dumps(line), flush=True)
 
 
+CG_METRIC = "C/G generator fwd+bwd tokens/s on 1 MI355X (GPT-2-small hidden state)"
+CG_KERNELS = ("cg_fwd", "cg_bwd")
+CG_SOURCES = ("cg.hip", "cg_internal.h")
+
+
+def cg_bytes_per_token(dm: int, H: int, elem: int) -> dict:
+    """Compulsory HBM bytes per token of the generator's passes: forward x in,
+    C and G out; backward x, dC, dG in, dx (float32) out (the weights and
+    their gradients are a few KB per launch)."""
+    return {"cg_fwd": dm * elem + 8 * H, "cg_bwd": dm * elem + 8 * H + dm * 4}
+
+
+def bench_cg(args):
+    import torch
+    import dynamic_head_composition_amd as ldc
+    from dynamic_head_composition_amd import cg
+    from dynamic_head_composition_amd import workloads as wl
+
+    ldc.load_library()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    cfg = dict(wl.CG_BENCH)
+    if args.tokens:
+        cfg["T"] = args.tokens
+        cfg["name"] += f"_trunc{args.tokens}"
+    log(f"generating generator workload {cfg} ...")
+    w = wl.make_cg_workload(**cfg)
+    x = w.torch_inputs("cuda")
+    T, dm, H = w.T, w.dm, w.H
+    elem = 2 if w.dtype == "bf16" else 4
+    f32 = dict(dtype=torch.float32, device="cuda")
+    cgo = (torch.empty((T, H), **f32), torch.empty((T, H), **f32))
+    grads = (torch.empty((T, dm), **f32), torch.empty((dm, H), **f32), torch.empty((dm, H), **f32))
+    ws = torch.empty(max(16, cg.workspace_bytes(0 if w.dtype == "bf16" else 1, T, dm, H)), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        cg.fwd(x["x"], x["wc"], x["wg"], out=cgo)
+        if evs:
+            evs[1].record()
+        cg.bwd(x["x"], x["wc"], x["wg"], x["dc"], x["dg"], out=grads, workspace=ws)
+        if evs:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if not all(bool(torch.isfinite(t).all()) for t in cgo + grads):
+        raise SystemExit("non-finite outputs")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kstat = {kn: stats_us([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])
+             for j, kn in enumerate(CG_KERNELS)}
+    bpt = cg_bytes_per_token(dm, H, elem)
+    per_kernel = {kn: {**kstat[kn], "alg_bytes_per_launch": bpt[kn] * T,
+                       "alg_GBps": round(bpt[kn] * T / (kstat[kn]["median_us"] * 1e-6) / 1e9, 1)}
+                  for kn in CG_KERNELS}
+    dominant = max(CG_KERNELS, key=lambda kn: kstat[kn]["median_us"])
+    achieved = per_kernel[dominant]["alg_GBps"]
+    value = T / (ms_per_step * 1e-3)
+    ceiling_tps = HBM_PEAK_GBPS * 1e9 / sum(bpt.values())
+    line = {
+        "metric": CG_METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "model_dim": dm, "heads": H, "recipe": w.recipe,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic([dominant], w.name, CG_SOURCES),
+                     "alg_bytes_per_launch": bpt[dominant] * T},
+        "step_hbm_ceiling_tokens_per_s": round(ceiling_tps, 1),
+        "step_roofline_frac": round(value / ceiling_tps, 4),
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        from oracle import cg_oracle as cgor
+        done, t_0, chunk = 0, time.perf_counter(), 4096
+        while done < T and time.perf_counter() - t_0 < args.cpu_budget:
+            lo, hi = done, min(T, done + chunk)
+            cgor.forward(w.x[lo:hi], w.wc, w.wg)
+            cgor.backward(w.x[lo:hi], w.wc, w.wg, w.dc[lo:hi], w.dg[lo:hi])
+            done = hi
+        el = time.perf_counter() - t_0
+        line["cpu_baseline"] = {"value": done / el, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+                                **host_cpu(),
+                                "sample": f"fp64 oracle forward+backward over tokens [0, {done}) in {chunk}-token "
+                                          f"slices (dW summed per slice); {el:.1f} s"}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def bench_mudd(args):
     import torch
     import dynamic_head_composition_amd as ldc
@@ -496,9 +601,10 @@ def main():
     # (measured: 5 warm-up steps read ~10% below 100); 100 steps take ~50 ms
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = GPT-2 small layer fwd+bwd)")
-    ap.add_argument("--workload", choices=("ldc", "dcmha", "mudd"), default="ldc",
+    ap.add_argument("--workload", choices=("ldc", "dcmha", "cg", "mudd"), default="ldc",
                     help="ldc: the Lightweight DC layer (default); dcmha: full DCMHA composition at "
-                         "the same shape; mudd: MUDD layer mixing")
+                         "the same shape; cg: the generator of C and G from the hidden state; "
+                         "mudd: MUDD layer mixing")
     ap.add_argument("--tokens", type=int, default=None, help="truncate the stream (quick runs only)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -516,6 +622,8 @@ def main():
         return bench_mudd(args)
     if args.workload == "dcmha":
         return bench_dcmha(args)
+    if args.workload == "cg":
+        return bench_cg(args)
 
     import torch
     import dynamic_head_composition_amd as ldc

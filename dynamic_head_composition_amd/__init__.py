@@ -77,6 +77,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for nm in ("dcmha_saved_bytes", "dcmha_bwd_workspace_bytes"):
         getattr(lib, nm).argtypes = [i32, i64, i32, i32, i32]
         getattr(lib, nm).restype = sz
+    lib.ldc_cg_fwd.argtypes = [i32, i64, i32, i32] + [vp] * 5 + [vp]
+    lib.ldc_cg_fwd.restype = i32
+    lib.ldc_cg_bwd.argtypes = [i32, i64, i32, i32] + [vp] * 8 + [vp, sz, vp]
+    lib.ldc_cg_bwd.restype = i32
+    lib.ldc_cg_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32]
+    lib.ldc_cg_bwd_workspace_bytes.restype = sz
     lib.mudd_fwd.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp, vp]
     lib.mudd_fwd.restype = i32
     lib.mudd_bwd.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]

@@ -356,6 +356,59 @@ DCMHA_BENCH = dict(T=65536, H=6, d=128, dtype="bf16", seed=5, docs=("geometric",
 
 
 # ----------------------------------------------------------------------------
+# Generator of the Lightweight DC weights (C = x WC, G = x WG)
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class CgWorkload:
+    name: str
+    T: int
+    dm: int
+    H: int
+    dtype: str
+    x: np.ndarray       # [T, dm] float32 (representable in `dtype`)
+    wc: np.ndarray      # [dm, H]
+    wg: np.ndarray      # [dm, H]
+    dc: np.ndarray      # [T, H] float32
+    dg: np.ndarray      # [T, H] float32
+    recipe: str = ""
+
+    def torch_inputs(self, device="cuda"):
+        import torch
+
+        def big(a):
+            if self.dtype == "bf16":
+                return torch.from_numpy(bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(device)
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+        f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return dict(x=big(self.x), wc=big(self.wc), wg=big(self.wg), dc=f(self.dc), dg=f(self.dg))
+
+
+def make_cg_workload(T: int, dm: int, H: int, *, dtype: str = "bf16", seed: int = 0,
+                     name: Optional[str] = None) -> CgWorkload:
+    """Seeded generator workload.  Draw order: x, WC, WG, dC, dG.  x rows are
+    RMS-normalised N(0, 1) (a normalised hidden state); WC ~ N(0, 0.5^2/dm)
+    so that C ~ N(0, 0.5^2) like the Lightweight DC recipe's C; WG ~ N(0, 1/dm);
+    dC, dG ~ N(0, 1).  x, WC, WG rounded to bf16 for bf16 workloads."""
+    assert dtype in ("bf16", "f32")
+    rng = np.random.default_rng(seed)
+    rnd = round_bf16 if dtype == "bf16" else (lambda a: a)
+    x = rnd(_rms_rows(_normal(rng, (T, dm))))
+    wc = rnd((0.5 / math.sqrt(dm) * _normal(rng, (dm, H))).astype(np.float32))
+    wg = rnd((1.0 / math.sqrt(dm) * _normal(rng, (dm, H))).astype(np.float32))
+    dc = _normal(rng, (T, H))
+    dg = _normal(rng, (T, H))
+    return CgWorkload(name=name or f"cg_T{T}_dm{dm}_H{H}_{dtype}_s{seed}", T=T, dm=dm, H=H, dtype=dtype,
+                      x=x, wc=wc, wg=wg, dc=dc, dg=dg,
+                      recipe=f"x=rms(N(0,1)) WC=N(0,0.25/dm) WG=N(0,1/dm) dC,dG=N(0,1) seed={seed}")
+
+
+# The generator's benchmark workload: the GPT-2 small hidden state feeding
+# the 6-head layer (model dim 768).
+CG_BENCH = dict(T=65536, dm=768, H=6, dtype="bf16", seed=6, name="cg_gpt2s_T65536_dm768_H6")
+
+
+# ----------------------------------------------------------------------------
 # MUDD layer mixing (AITNT page, section "第一刀—砍层间")
 # ----------------------------------------------------------------------------
 @dataclasses.dataclass
