@@ -256,12 +256,11 @@ def dcmha_design_bytes_per_token(H: int, d: int, elem: int) -> dict:
     """Bytes per token each DCMHA kernel moves as designed: its operands once,
     float32 O and gradients, and the per-head bands the kernels hand each
     other (512 B per token and head each): P and R saved by the forward, P
-    read twice by bwd_q (the mixing passes), dS written by bwd_q and read by
-    bwd_kv with R."""
+    read by bwd_q, dS written by bwd_q and read by bwd_kv with R."""
     row, comp, band = H * d, 4 * H * H, 512 * H
     return {
         "dcmha_fwd": 3 * row * elem + 2 * comp + 4 + row * 4 + 2 * band,
-        "dcmha_bwd_q": 4 * row * elem + 2 * comp + 4 + 2 * band + row * 4 + 2 * comp + band,
+        "dcmha_bwd_q": 4 * row * elem + 2 * comp + 4 + band + row * 4 + 2 * comp + band,
         "dcmha_bwd_kv": 2 * row * elem + 4 + 2 * band + 2 * row * 4,
     }
 
@@ -329,6 +328,8 @@ def bench_dcmha(args):
         if evs:
             evs[3].record()
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -405,7 +406,7 @@ def bench_dcmha(args):
 
 CG_METRIC = "C/G generator fwd+bwd tokens/s on 1 MI355X (GPT-2-small hidden state)"
 CG_KERNELS = ("cg_fwd", "cg_bwd")
-CG_SOURCES = ("cg.hip", "cg_internal.h")
+CG_SOURCES = ("ldc_device.hpp", "cg.hip", "cg_internal.h")
 
 
 def cg_bytes_per_token(dm: int, H: int, elem: int) -> dict:
@@ -449,6 +450,8 @@ def bench_cg(args):
         if evs:
             evs[2].record()
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

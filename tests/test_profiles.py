@@ -1,5 +1,9 @@
 """Consistency of the committed rocprofv3 traffic record with the code (CPU).
 
+Workloads: the Lightweight DC configurations, the DCMHA composition, the C/G
+generator and MUDD mixing, each with the kernel sources its entries were
+taken on.
+
 profiles/hbm_traffic.json holds measured HBM bytes per launch, tagged with a
 digest of the kernel sources they were taken on; bench.py reports them only
 while the digest matches.  For every pass of the layer whose launches all have
@@ -30,6 +34,14 @@ def design(workload: str) -> dict:
         c = wl.MUDD_BENCH
         bpt = bench.mudd_bytes_per_token(c["dm"], c["W"], c["J"], 2 if c["dtype"] == "bf16" else 4)
         return {k: v * c["T"] for k, v in bpt.items()}
+    if workload.startswith("dcmha_"):
+        c = wl.DCMHA_BENCH
+        bpt = bench.dcmha_design_bytes_per_token(c["H"], c["d"], 2 if c["dtype"] == "bf16" else 4)
+        return {k: v * c["T"] for k, v in bpt.items()}
+    if workload.startswith("cg_"):
+        c = wl.CG_BENCH
+        bpt = bench.cg_bytes_per_token(c["dm"], c["H"], 2 if c["dtype"] == "bf16" else 4)
+        return {k: v * c["T"] for k, v in bpt.items()}
     cfg = ldc_config(workload)
     bpt = bench.design_bytes_per_token(cfg["H"], cfg["d"], 2 if cfg["dtype"] == "bf16" else 4)
     return {k: v * cfg["T"] for k, v in bpt.items()}
@@ -45,7 +57,13 @@ def entries():
 
 
 def sources(kernel):
-    return bench.MUDD_SOURCES if kernel.startswith("mudd_") else bench.SOURCES
+    if kernel.startswith("mudd_"):
+        return bench.MUDD_SOURCES
+    if kernel.startswith("dcmha_"):
+        return bench.DCMHA_SOURCES
+    if kernel.startswith("cg_"):
+        return bench.CG_SOURCES
+    return bench.SOURCES
 
 
 @pytest.mark.parametrize("workload,kernel,ent", list(entries()), ids=lambda x: x if isinstance(x, str) else "")
@@ -63,7 +81,7 @@ def test_traffic_record(workload, kernel, ent):
 def pass_cases():
     rec = json.load(open(REC))
     for workload in rec:
-        if workload.startswith("mudd_"):
+        if workload.startswith(("mudd_", "dcmha_", "cg_")):
             continue
         for pn in bench.PASSES:
             yield workload, pn
