@@ -14,7 +14,7 @@ constexpr int kVersion = 10000;  // 1.0.0
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool head_dim_supported(int dtype, int d) {
-  if (dtype == LDC_BF16) return d == 64 || d == 128;
+  if (dtype == LDC_BF16) return d == 16 || d == 64 || d == 128;
   return d == 16 || d == 64 || d == 128;
 }
 

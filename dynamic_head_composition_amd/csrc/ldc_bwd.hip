@@ -39,7 +39,10 @@ __global__ __launch_bounds__(NW * kWave) void bwd_q_kernel(const BwdArgs a) {
   constexpr int BQ = 16 * NW;
   constexpr int kHalo = halo_rows<NB>();
   constexpr int kBandWords = band_words<NB>();
-  constexpr int R = BQ + kHalo;
+  // tile rows: the span, rounded up to whole DMA instructions (32-byte rows
+  // fill 32 rows per instruction)
+  constexpr int R = (BQ + kHalo + Tile<T, D>::rows_per_inst - 1) / Tile<T, D>::rows_per_inst *
+                    Tile<T, D>::rows_per_inst;
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
   __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
@@ -295,7 +298,9 @@ __global__ __launch_bounds__(NW * kWave) void bwd_kv_kernel(const BwdArgs a) {
   constexpr int BK = 16 * NW;
   constexpr int kHalo = halo_rows<NB>();
   constexpr int kBandWords = band_words<NB>();
-  constexpr int R = BK + kHalo;  // query rows [k0, k0 + BK + kHalo)
+  // query rows [k0, k0 + BK + kHalo), rounded up to whole DMA instructions
+  constexpr int R = (BK + kHalo + Tile<T, D>::rows_per_inst - 1) / Tile<T, D>::rows_per_inst *
+                    Tile<T, D>::rows_per_inst;
   constexpr int RP = (R + 63) / 64 * 64;
   // per-row scalars of the staged head: C, G, dC, row max, 1/row sum
   enum { SC_C = 0, SC_G = 1, SC_DC = 2, SC_MX = 3, SC_INV = 4, NSC = 5 };
@@ -543,6 +548,7 @@ hipError_t bwd_dispatch(int dtype, int d, const BwdArgs& a, int parts, hipStream
   if (dtype == 0) {
     if (d == 128) return wide ? launch_bwd<bf16_t, 128, 4, 10>(a, parts, st) : launch_bwd<bf16_t, 128, 8, 8>(a, parts, st);
     if (d == 64) return wide ? launch_bwd<bf16_t, 64, 4, 10>(a, parts, st) : launch_bwd<bf16_t, 64, 8, 8>(a, parts, st);
+    if (d == 16) return wide ? launch_bwd<bf16_t, 16, 4, 10>(a, parts, st) : launch_bwd<bf16_t, 16, 8, 8>(a, parts, st);
   } else {
     if (d == 128 && !wide) return launch_bwd<float, 128, 2, 8>(a, parts, st);
     if (d == 64) return wide ? launch_bwd<float, 64, 4, 10>(a, parts, st) : launch_bwd<float, 64, 4, 8>(a, parts, st);

@@ -43,6 +43,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // storage of one bfloat16
 typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
@@ -101,7 +102,11 @@ struct Tile {
   static constexpr int rows_per_inst = 64 / chunks;  // rows one wave-wide DMA fills
   // chunk position of logical chunk c in row r
   static __device__ __forceinline__ int pos(int r, int c) {
-    if constexpr (Elem<T>::bf16 && D == 128) {
+    if constexpr (Elem<T>::bf16 && D == 16) {
+      // 32-byte rows: a 16-row block is one contiguous 512-byte region, read
+      // conflict-free by both patterns without a swizzle
+      return c;
+    } else if constexpr (Elem<T>::bf16 && D == 128) {
       // row bits 0, 1, 2, 3 -> chunk bits 0, 2, 3, 1
       return c ^ ((r & 1) | ((r & 6) << 1) | ((r >> 2) & 2));
     } else if constexpr (Elem<T>::bf16 && D == 64) {
@@ -120,12 +125,19 @@ struct Tile {
   }
 };
 
+// bf16 rows of 16 elements contract on v_mfma_f32_16x16x16_bf16 (K = 16, four
+// bf16 values per lane); wider bf16 rows on the K = 32 instruction.
+template <typename T, int D>
+constexpr bool kNarrow = Elem<T>::bf16 && D == 16;
+
 // Number of 32-bit registers the lane needs for one row's d-slice.
 template <typename T, int D>
 struct RowFrag {
-  // bf16: D/32 chunks of 8 values; fp32: D/4 values (one per 16x16x4 step)
-  static constexpr int n = Elem<T>::bf16 ? D / 32 : D / 4;
-  typename std::conditional<Elem<T>::bf16, bf16x8, float>::type v[n];
+  // bf16: D/32 chunks of 8 values (D = 16: one piece of 4); fp32: D/4 values
+  // (one per 16x16x4 step)
+  static constexpr int n = kNarrow<T, D> ? 1 : Elem<T>::bf16 ? D / 32 : D / 4;
+  typename std::conditional<kNarrow<T, D>, bf16x4,
+                            typename std::conditional<Elem<T>::bf16, bf16x8, float>::type>::type v[n];
 };
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -139,6 +151,11 @@ __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mma(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
+                                                    0, 0, 0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -347,7 +364,11 @@ __device__ __forceinline__ void wait_dma() {
 // NT: non-temporal loads (the caller reads each such row once).
 template <typename T, int D, bool NT = false>
 __device__ __forceinline__ void load_row_frag(RowFrag<T, D>& f, const T* __restrict__ row, int g) {
-  if constexpr (Elem<T>::bf16) {
+  if constexpr (kNarrow<T, D>) {
+    // d = 4g .. 4g+3
+    const u32x2* src = reinterpret_cast<const u32x2*>(row + 4 * g);
+    f.v[0] = __builtin_bit_cast(bf16x4, NT ? __builtin_nontemporal_load(src) : *src);
+  } else if constexpr (Elem<T>::bf16) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
       const u32x4* src = reinterpret_cast<const u32x4*>(row + 32 * kk + 8 * g);
@@ -370,12 +391,17 @@ __device__ __forceinline__ void load_row_frag(RowFrag<T, D>& f, const T* __restr
 template <typename T, int D>
 struct LaneOffsets {
   using TL = Tile<T, D>;
-  static constexpr int ND = Elem<T>::bf16 ? D / 32 : D / 16;  // score-operand reads per row
-  static constexpr int NT = Elem<T>::bf16 ? D / 32 : 1;       // transpose-read column groups
+  static constexpr int ND = kNarrow<T, D> ? 1 : Elem<T>::bf16 ? D / 32 : D / 16;  // score reads per row
+  static constexpr int NT = kNarrow<T, D> ? 1 : Elem<T>::bf16 ? D / 32 : 1;       // transpose column groups
   int dk[ND];  // score operand: row n of the block, chunk of k-step kk
   int tr[NT];  // value operand (bf16): row 4g + n/4, chunk 4p + n%4, half (n/4)%2 (for e = 0)
   __device__ __forceinline__ LaneOffsets(int g, int n) {
-    if constexpr (Elem<T>::bf16) {
+    if constexpr (kNarrow<T, D>) {
+      // score operand: 8 bytes of row n at d = 4g; value operand: lane supplies
+      // row 4g + n/4 at d = 4(n%4), so that lane q receives d = q of 4 rows
+      dk[0] = n * TL::row_bytes + 8 * g;
+      tr[0] = (4 * g + (n >> 2)) * TL::row_bytes + 8 * (n & 3);
+    } else if constexpr (Elem<T>::bf16) {
 #pragma unroll
       for (int kk = 0; kk < ND; ++kk) dk[kk] = n * TL::row_bytes + TL::pos(n, 4 * kk + g) * 16;
       const int rr = n >> 2, bq = n & 3, row = 4 * g + rr;
@@ -397,7 +423,10 @@ __device__ __forceinline__ f32x4 mma_dcontract(f32x4 acc, const T* tile, int row
                                                const LaneOffsets<T, D>& lo, const RowFrag<T, D>& f) {
   using TL = Tile<T, D>;
   const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
-  if constexpr (Elem<T>::bf16) {
+  if constexpr (kNarrow<T, D>) {
+    const uint2 u = *reinterpret_cast<const uint2*>(base + lo.dk[0]);
+    acc = mma(__builtin_bit_cast(bf16x4, u), f.v[0], acc);
+  } else if constexpr (Elem<T>::bf16) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
       uint4 u = *reinterpret_cast<const uint4*>(base + lo.dk[kk]);
@@ -459,9 +488,9 @@ struct BandOperand<float, NB> {
 
 // Offset (elements) of the 4 consecutive d-values a lane holds in acc[r] of
 // mma_tcontract's result (the lane's group g; layout given there).
-template <typename T>
+template <typename T, int D>
 __device__ __forceinline__ int tcontract_d(int r, int g) {
-  if constexpr (Elem<T>::bf16)
+  if constexpr (Elem<T>::bf16 && !kNarrow<T, D>)
     return 32 * (r >> 1) + 8 * g + 4 * ((r & 1) ^ (g & 1));
   else
     return 16 * r + 4 * g;
@@ -526,14 +555,14 @@ __device__ __forceinline__ void store_slice(const PendingRow& pr, const f32x4& a
 template <typename T, int D>
 __device__ __forceinline__ void store_row(const PendingRow& pr, const f32x4 (&acc)[D / 16], int g,
                                           int n) {
-  if constexpr (Elem<T>::bf16) {
+  if constexpr (Elem<T>::bf16 && !kNarrow<T, D>) {
     if (pr.nrows > 0)
 #pragma unroll
       for (int p = 0; p < D / 32; ++p) store_slice(pr, acc[2 * p], acc[2 * p + 1], p, g, n);
   } else {
     if (pr.on)
 #pragma unroll
-      for (int r = 0; r < D / 16; ++r) store4(pr.row + tcontract_d<T>(r, g), acc[r], pr.scale);
+      for (int r = 0; r < D / 16; ++r) store4(pr.row + tcontract_d<T, D>(r, g), acc[r], pr.scale);
   }
 }
 
@@ -560,7 +589,7 @@ template <int P>
 using Part = std::integral_constant<int, P>;
 template <typename T, int D>
 constexpr int tcontract_groups() {
-  return Elem<T>::bf16 ? D / 32 : 1;
+  return (Elem<T>::bf16 && !kNarrow<T, D>) ? D / 32 : 1;
 }
 struct NoHook {
   template <typename P>
@@ -573,7 +602,29 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
                                               Hook&& hook = Hook{}) {
   using TL = Tile<T, D>;
   const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
-  if constexpr (Elem<T>::bf16) {
+  if constexpr (kNarrow<T, D>) {
+    // K = 16 steps: one transpose read per 16-token block (rows 4g..4g+3 of
+    // the block for lane group g), contracted with that block's half of the
+    // band operand's hi and lo chunks
+    typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+    if (prev.on) store4(prev.row + tcontract_d<T, D>(0, g), acc[0], prev.scale);
+    store_fence();
+    acc[0] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NB / 2; ++ks) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_v4*)(base + lo.tr[0] + (32 * ks + 16 * half) * TL::row_bytes));
+        const bf16x4 ph = half ? __builtin_shufflevector(P.hi[ks], P.hi[ks], 4, 5, 6, 7)
+                               : __builtin_shufflevector(P.hi[ks], P.hi[ks], 0, 1, 2, 3);
+        const bf16x4 pl = half ? __builtin_shufflevector(P.lo[ks], P.lo[ks], 4, 5, 6, 7)
+                               : __builtin_shufflevector(P.lo[ks], P.lo[ks], 0, 1, 2, 3);
+        acc[0] = mma(x, ph, acc[0]);
+        acc[0] = mma(x, pl, acc[0]);
+      }
+    }
+  } else if constexpr (Elem<T>::bf16) {
     typedef __attribute__((address_space(3))) bf16x4 lds_v4;
     constexpr int NP = D / 32;  // column groups of 32
     constexpr int PG = 1;       // column groups per store group
@@ -611,7 +662,7 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
   } else {
     if (prev.on)
 #pragma unroll
-      for (int r = 0; r < D / 16; ++r) store4(prev.row + tcontract_d<T>(r, g), acc[r], prev.scale);
+      for (int r = 0; r < D / 16; ++r) store4(prev.row + tcontract_d<T, D>(r, g), acc[r], prev.scale);
     store_fence();
 #pragma unroll
     for (int r = 0; r < D / 16; ++r) acc[r] = zero4();

@@ -38,7 +38,10 @@ __global__ __launch_bounds__(NW * kWave, (D == 64 && Elem<T>::bf16 && NB == 8) ?
     const FwdArgs a) {
   constexpr int BQ = 16 * NW;
   constexpr int kHalo = halo_rows<NB>();
-  constexpr int R = BQ + kHalo;
+  // tile rows: the span, rounded up to whole DMA instructions (32-byte rows
+  // fill 32 rows per instruction)
+  constexpr int R = (BQ + kHalo + Tile<T, D>::rows_per_inst - 1) / Tile<T, D>::rows_per_inst *
+                    Tile<T, D>::rows_per_inst;
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
   __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
@@ -256,6 +259,7 @@ hipError_t fwd_dispatch(int dtype, int d, const FwdArgs& a, bool value, hipStrea
   if (dtype == 0) {
     if (d == 128) return wide ? launch_fwd<bf16_t, 128, 4, 10>(a, value, st) : launch_fwd<bf16_t, 128, 8, 8>(a, value, st);
     if (d == 64) return wide ? launch_fwd<bf16_t, 64, 4, 10>(a, value, st) : launch_fwd<bf16_t, 64, 8, 8>(a, value, st);
+    if (d == 16) return wide ? launch_fwd<bf16_t, 16, 4, 10>(a, value, st) : launch_fwd<bf16_t, 16, 8, 8>(a, value, st);
   } else {
     if (d == 128 && !wide) return launch_fwd<float, 128, 2, 8>(a, value, st);
     if (d == 64) return wide ? launch_fwd<float, 64, 4, 10>(a, value, st) : launch_fwd<float, 64, 4, 8>(a, value, st);

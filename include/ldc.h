@@ -24,8 +24,8 @@
  *   C, G, dC, dG               : [T, H] float32 row-major;
  *   doc_ids                    : [T] int32, any values (only equality matters).
  * Pointers are DEVICE pointers owned by the caller; base addresses must be
- * 16-byte aligned.  Supported shapes: d in {64, 128} for LDC_BF16 and
- * d in {16, 64, 128} for LDC_F32; 1 <= window <= 128 (LDC_F32 with d = 128:
+ * 16-byte aligned.  Supported shapes: d in {16, 64, 128} for both dtypes;
+ * 1 <= window <= 128 (LDC_F32 with d = 128:
  * up to 113, else LDC_ERR_UNSUPPORTED); H >= 1; T >= 0 (T == 0 is a no-op);
  * T*H*d < 2^31.
  *

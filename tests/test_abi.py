@@ -54,7 +54,8 @@ def test_workspace_and_saved_bytes():
     assert ldc.workspace_bytes(ldc.LDC_F32, 17, 3, 16, 5) == room(2 * 8192 + 17 * 3 * 8) + 2 * 8192
     assert ldc.saved_bytes(ldc.LDC_F32, 17, 2, 16, 112) == 2 * 2048 * 4 + 17 * 2 * 8
     assert ldc.workspace_bytes(ldc.LDC_BF16, 0, 6, 128, 112) == 0
-    assert ldc.workspace_bytes(ldc.LDC_BF16, 10, 6, 16, 112) == 0  # unsupported -> 0
+    assert ldc.workspace_bytes(ldc.LDC_BF16, 10, 6, 32, 112) == 0  # unsupported -> 0
+    assert ldc.workspace_bytes(ldc.LDC_BF16, 10, 6, 16, 112) == room(8192 + 10 * 6 * 8) + 8192
     # windows above 113 keys: bands of 10 key blocks (2,560 words per 16-query block)
     wide = 4096 * 2560 * 4
     assert ldc.saved_bytes(ldc.LDC_BF16, 65536, 6, 128, 128) == wide + 65536 * 6 * 8
@@ -114,7 +115,7 @@ def test_validation_errors(call):
     assert call(scale=float("inf")) == 2
     assert call(scale=float("nan")) == 2
     assert call(d=32) == 5                         # LDC_ERR_UNSUPPORTED
-    assert call(dtype=ldc.LDC_BF16, d=16) == 5
+    assert call(d=256) == 5
     nptr = 7 if call is fwd_call else 12
     for i in range(nptr):
         ptrs = [A] * nptr

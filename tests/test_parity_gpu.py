@@ -55,6 +55,13 @@ SMALL = [  # (T, H, d, dtype, window, docs, seed)
     (150, 1, 128, "bf16", 112, ("geometric", 50), 26),
     (97, 1, 64, "bf16", 20, ("uniform", 8, 30), 27),
     (300, 16, 64, "bf16", 112, ("geometric", 80), 28),
+    # bf16 rows of 16 (the K = 16 MFMA paths): the tiny configuration's shape
+    # in bf16, ragged streams, several tiles, windows 1 and 113
+    (256, 2, 16, "bf16", 112, ("fixed", np.array([0] * 100 + [1] * 156, dtype=np.int32)), 29),
+    (17, 3, 16, "bf16", 112, ("geometric", 6), 30),
+    (1000, 6, 16, "bf16", 113, ("geometric", 200), 31),
+    (333, 4, 16, "bf16", 1, ("uniform", 8, 64), 32),
+    (4096, 12, 16, "bf16", 112, ("geometric", 1024), 33),
 ]
 
 
@@ -332,6 +339,7 @@ WIDE = [  # windows of 114..128 keys (10-block bands): (T, H, d, dtype, window, 
     (1000, 12, 64, "bf16", 120, ("single",), 44),
     (129, 1, 128, "bf16", 127, ("single",), 45),
     (700, 5, 64, "bf16", 116, ("geometric", 150), 46),
+    (600, 6, 16, "bf16", 128, ("geometric", 200), 49),
     (4096, 6, 128, "bf16", 128, ("geometric", 1024), 47),
 ]
 
