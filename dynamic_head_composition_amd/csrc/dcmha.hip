@@ -18,25 +18,28 @@
 // all heads' 16 x 128 bands of its queries in registers (HM x 32 per lane):
 // the query-side kernels run one wave per SIMD (4 waves, 64 queries per
 // workgroup) with up to 512 registers per lane.  Tiles of one head at a time
-// stream into LDS by DMA, double-buffered, as in the Lightweight DC kernels.
+// stream into LDS by DMA: through three buffers in the query-side kernels
+// (one workgroup per CU, so each tile's DMA gets two stages of lead), two in
+// the key-side one.
 //  * fwd    (query-centric): K phase (raw scores of each source head composed
 //           into every target's Z), softmax of every target in registers, V
 //           phase (R_h from all heads' P, then O_h).  Saves P and R bands.
-//  * bwd_q  (query-centric): V phase (dR of every head, unrolled so each
-//           head's band has its own registers), VALU mixing (dCW, dP, dZ with
-//           the saved P), K phase (raw scores for dCS; dS, dQ; dS bands saved
+//  * bwd_q  (query-centric): V phase (dR of each head, mixed as soon as it
+//           is complete into dCW and the running dP of every head, with the
+//           saved P), dZ, K phase (raw scores for dCS; dS, dQ; dS bands saved
 //           for the key side).
 //  * bwd_kv (key-centric): dV_h = R_h^T dO_h and dK_h = scale dS_h^T Q_h from
 //           the bands: token contractions only.
 // Bands: one 2,048-word block per 16-query block qb and head h, at word
-// (qb*H + h) * kBandWords.  The R and dS bands, read by the key-centric
-// kernel, use the Lightweight DC layout ([key block][key 16][query 16]: a
-// key-centric lane reads its 4 queries as one 16-byte word group).  The P
-// band is read only by query-centric waves and is stored query-major
-// ([key block][query 16][key 16]): lane (g, n) holds keys 4g..4g+3 of block
-// b, one 16-byte piece at word b*256 + n*16 + 4g, so it is written and read
-// as whole 1 KB lines per block.  Deterministic: no atomics, every output
-// element written once.
+// (qb*H + h) * kBandWords, of plain fp32 words (a band that feeds an MFMA is
+// split into bf16 high and low parts where it is loaded).  The R and dS
+// bands, read by the key-centric kernel, use the Lightweight DC layout ([key
+// block][key 16][query 16]: a key-centric lane reads its 4 queries as one
+// 16-byte word group).  The P band is read only by query-centric waves and is
+// stored query-major ([key block][query 16][key 16]): lane (g, n) holds keys
+// 4g..4g+3 of block b, one 16-byte piece at word b*256 + n*16 + 4g, so it is
+// written and read as whole 1 KB lines per block.  Deterministic: no atomics,
+// every output element written once.
 #include "dcmha_internal.h"
 #include "ldc_device.hpp"
 #include "ldc_pipeline.hpp"
@@ -48,16 +51,24 @@ __device__ __forceinline__ float comp_at(const float* x, int t, int H, int row, 
   return x[((size_t)t * H + row) * H + col];
 }
 
+// comp_at when ok, else 0, with the load itself unconditional (from entry
+// (0, 0) when !ok): a load under a branch is waited for inside the branch,
+// which serialises a row of such loads on the memory latency.
+__device__ __forceinline__ float comp_or0(const float* x, int t, int H, int row, int col, bool ok) {
+  const float v = comp_at(x, t, H, ok ? row : 0, ok ? col : 0);
+  return ok ? v : 0.f;
+}
+
 // Write one wave's 16 x 128 band block (accumulator layout, lane (g, n) holds
 // words (4g+i)*16 + n of key block b) as 4-byte words.
-template <typename T, bool ENCODE>
+template <typename T>
 __device__ __forceinline__ void write_band(uint32_t* blk, const f32x4 (&x)[kKeyBlocks], float* xp,
                                            int g, int n) {
   uint32_t wv[kKeyBlocks][4];
 #pragma unroll
   for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv[b][i] = ENCODE ? band_encode<T>(x[b][i]) : __float_as_uint(x[b][i]);
+    for (int i = 0; i < 4; ++i) wv[b][i] = __float_as_uint(x[b][i]);
   if constexpr (Elem<T>::bf16) {
     store_band_block(blk, wv, xp, g, n);
   } else {
@@ -79,6 +90,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
   constexpr int R = BQ + kHalo;
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
+  __shared__ __attribute__((aligned(1024))) T s_x2[R * D];
   __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
   __shared__ __attribute__((aligned(16))) float s_xp[Elem<T>::bf16 ? NW * 512 : 4];
 
@@ -96,40 +108,52 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
   const bool tval = t < a.T;
   const int tc = tval ? t : a.T - 1;
   const int H = a.H;
-  const int Hp = (H + 1) & ~1;
+  const int Hp = (H + 2) / 3 * 3;
+  constexpr int NIW = tile_insts_per_wave<T, D, R, NW>();
   const int qb = (q0 >> 4) + w;
   const bool wval = q0 + 16 * w < a.T;
   const bool save = a.pband != nullptr;
   float* xp = s_xp + (Elem<T>::bf16 ? w * 512 : 0);
   const LaneOffsets<T, D> lo(g, n);
 
-  // phases: 0 = K (scores), 1 = V (values; nothing loaded when !OUT)
-  auto issue = [&](int phase, int h, bool on, auto bc) {
-    T* buf = decltype(bc)::value == 0 ? s_x0 : s_x1;
-    issue_tile<T, D, R, NW>(buf, phase == 0 ? k : v, span0, a.T, H, h, on && (phase == 0 || OUT));
+  // phases: 0 = K (scores), 1 = V (values; nothing loaded when !OUT).
+  // Three LDS buffers: stage j reads buffer j%3 and issues the DMA of stage
+  // j+2 into buffer (j+2)%3, which stage j-1 has finished reading.
+  auto buffer = [&](auto bc) -> T* {
+    constexpr int B = decltype(bc)::value;
+    return B == 0 ? s_x0 : (B == 1 ? s_x1 : s_x2);
   };
-  auto issue_next = [&](int phase, int j, auto bc) {
-    const NextStage ns = next_stage(phase, j, H, Hp, 2);
-    issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<1 - decltype(bc)::value>{});
+  auto issue = [&](int phase, int h, bool on, auto bc) {
+    issue_tile<T, D, R, NW>(buffer(bc), phase == 0 ? k : v, span0, a.T, H, h, on && (phase == 0 || OUT));
+  };
+  auto issue_ahead = [&](int phase, int j, auto bc) {
+    const NextStage ns = stage_after_next(phase, j, H, Hp, 2);
+    issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<(decltype(bc)::value + 2) % 3>{});
   };
   // column h' of CS[t] (every target h), pre-scaled by the softmax scale
   auto load_cs = [&](float (&dst)[HM], int hs) {
 #pragma unroll
-    for (int h = 0; h < HM; ++h) dst[h] = h < H ? a.scale * comp_at(a.cs, tc, H, h, hs) : 0.f;
+    for (int h = 0; h < HM; ++h) dst[h] = a.scale * comp_or0(a.cs, tc, H, h, hs, h < H);
   };
   // row h of CW[t] (every source h')
   auto load_cw = [&](float (&dst)[HM], int ht) {
 #pragma unroll
-    for (int h = 0; h < HM; ++h) dst[h] = h < H ? comp_at(a.cw, tc, H, ht, h) : 0.f;
+    for (int h = 0; h < HM; ++h) dst[h] = comp_or0(a.cw, tc, H, ht, h, h < H);
   };
 
+  // Register operands rotate with the buffers: stage j uses slot j%3 and
+  // loads slot (j+1)%3 before it issues its DMA.  The V phase's first CW row
+  // is loaded here, so that no load is issued between the DMAs of the last
+  // K stages and the first V stage.
+  RowFrag<T, D> qfb[3];
+  float csb[3][HM], cwb[3][HM];
   issue(0, 0, true, Buf<0>{});
   issue_doc<R, NW>(s_doc, a.doc, span0, a.T);
-  RowFrag<T, D> qfb[2];
-  float csb[2][HM];
   load_row_frag<T, D, true>(qfb[0], q + (size_t)tc * H * D, g);
   load_cs(csb[0], 0);
-  wait_dma();
+  load_cw(cwb[0], 0);
+  issue(0, 1, 1 < H, Buf<1>{});
+  wait_dma_except<NIW>();
 
   uint32_t mbits = 0;
   {
@@ -144,26 +168,34 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
         mbits |= (ok ? 1u : 0u) << (4 * b + i);
       }
   }
-  const uint32_t full = full_blocks(mbits);
-
-  // composed scores Z_h of every target head (then P_h in place)
+  // composed scores Z_h of every target head (then P_h in place), started
+  // at 0 where the key is admitted and at -inf where it is not: the finite
+  // score terms leave -inf in place, so Z is masked without a separate pass
   f32x4 z[HM][kKeyBlocks];
+  {
+    f32x4 z0[kKeyBlocks];
 #pragma unroll
-  for (int h = 0; h < HM; ++h)
+    for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) z[h][b] = zero4();
+      for (int i = 0; i < 4; ++i) z0[b][i] = ((mbits >> (4 * b + i)) & 1u) ? 0.f : -INFINITY;
+#pragma unroll
+    for (int h = 0; h < HM; ++h)
+#pragma unroll
+      for (int b = 0; b < kKeyBlocks; ++b) z[h][b] = z0[b];
+  }
 
   // ---- phase 0 (K_h' staged): Z_h += scale CS[t,h,h'] Q_h' K_h'^T ----
-  for_stage_pairs(Hp, [&](int j, auto bc) {
+  for_stage_triples(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
-    const T* cur = B == 0 ? s_x0 : s_x1;
-    wait_dma();
+    constexpr int B1 = (B + 1) % 3;
+    const T* cur = buffer(bc);
+    wait_dma_except<NIW>();
     const bool real = j < H;
     const int hn = j + 1 < H ? j + 1 : 0;
-    load_row_frag<T, D, true>(qfb[1 - B], q + ((size_t)tc * H + hn) * D, g);
-    load_cs(csb[1 - B], hn);
+    load_row_frag<T, D, true>(qfb[B1], q + ((size_t)tc * H + hn) * D, g);
+    load_cs(csb[B1], hn);
     __builtin_amdgcn_sched_barrier(0);
-    issue_next(0, j, bc);
+    issue_ahead(0, j, bc);
     if (!real) return;
     __builtin_amdgcn_s_setprio(2);
     f32x4 s[kKeyBlocks];
@@ -186,7 +218,6 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
   static_for<0, HM>([&](auto hc) {
     constexpr int h = decltype(hc)::value;
     if (h < H) {
-      mask_band(z[h], mbits, full, -INFINITY);
       float mx = -INFINITY;
 #pragma unroll
       for (int b = 0; b < kKeyBlocks; ++b)
@@ -211,17 +242,13 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
         uint32_t* blk = a.pband + ((size_t)qb * H + h) * kBandWords;
 #pragma unroll
         for (int b = 0; b < kKeyBlocks; ++b)
-          __builtin_nontemporal_store(
-              u32x4{band_encode<T>(z[h][b][0]), band_encode<T>(z[h][b][1]), band_encode<T>(z[h][b][2]),
-                    band_encode<T>(z[h][b][3])},
-              reinterpret_cast<u32x4*>(blk + b * 256 + n * 16 + 4 * g));
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, z[h][b]),
+                                      reinterpret_cast<u32x4*>(blk + b * 256 + n * 16 + 4 * g));
       }
     }
   });
 
   // ---- phase 1 (V_h staged): R_h = sum_h' CW[t,h,h'] P_h', O_h = R_h V_h ----
-  float cwb[2][HM];
-  load_cw(cwb[0], 0);
   f32x4 pend[D / 16];
   int pend_h = -1;
   auto pending = [&]() {
@@ -231,14 +258,14 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
     if constexpr (OUT) store_row<T, D>(pending(), pend, g, n);
     pend_h = -1;
   };
-  for_stage_pairs(Hp, [&](int j, auto bc) {
+  for_stage_triples(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
-    const T* cur = B == 0 ? s_x0 : s_x1;
-    wait_dma();
+    const T* cur = buffer(bc);
+    wait_dma_except<NIW>();
     const bool real = j < H;
-    load_cw(cwb[1 - B], j + 1 < H ? j + 1 : 0);
+    load_cw(cwb[(B + 1) % 3], j + 1 < H ? j + 1 : 0);
     __builtin_amdgcn_sched_barrier(0);
-    issue_next(1, j, bc);
+    issue_ahead(1, j, bc);
     if (!real) {
       flush();
       return;
@@ -256,7 +283,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
           for (int i = 0; i < 4; ++i) r[b][i] = fmaf(c, z[h][b][i], r[b][i]);
       }
     });
-    if (save && wval) write_band<T, true>(a.rband + ((size_t)qb * H + j) * kBandWords, r, xp, g, n);
+    if (save && wval) write_band<T>(a.rband + ((size_t)qb * H + j) * kBandWords, r, xp, g, n);
     if constexpr (OUT) {
       BandOperand<T> op;
       op.set(r);
@@ -277,10 +304,14 @@ template <typename T, int D, int NW, int HM>
 __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdArgs a) {
   constexpr int BQ = 16 * NW;
   constexpr int R = BQ + kHalo;
-  constexpr int HMp = HM;
-  static_assert(HM % 2 == 0, "the V phase is unrolled in stage pairs");
+  constexpr int HM3 = (HM + 2) / 3 * 3;
+  constexpr int NIW = tile_insts_per_wave<T, D, R, NW>();
+  constexpr int kCompFloats = BQ * HM * HM;  // the CS or CW rows of the tile's queries
   __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
   __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
+  __shared__ __attribute__((aligned(1024))) T s_x2[R * D];
+  __shared__ __attribute__((aligned(16))) float s_cw[(kCompFloats + 63) / 64 * 64];
+  __shared__ __attribute__((aligned(16))) float s_cs[(kCompFloats + 63) / 64 * 64];
   __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
   __shared__ __attribute__((aligned(16))) float s_xp[Elem<T>::bf16 ? NW * 512 : 4];
 
@@ -299,20 +330,24 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
   const bool tval = t < a.T;
   const int tc = tval ? t : a.T - 1;
   const int H = a.H;
-  const int Hp = (H + 1) & ~1;
+  const int Hp = (H + 2) / 3 * 3;
   const int qb = (q0 >> 4) + w;
   const bool wval = q0 + 16 * w < a.T;
   float* xp = s_xp + (Elem<T>::bf16 ? w * 512 : 0);
   const LaneOffsets<T, D> lo(g, n);
 
-  // phases: 0 = V (dR), 1 = K (dCS, dS, dQ)
-  auto issue = [&](int phase, int h, bool on, auto bc) {
-    T* buf = decltype(bc)::value == 0 ? s_x0 : s_x1;
-    issue_tile<T, D, R, NW>(buf, phase == 0 ? v : k, span0, a.T, H, h, on);
+  // phases: 0 = V (dR), 1 = K (dCS, dS, dQ).  Three LDS buffers: stage j
+  // reads buffer j%3 and issues the DMA of stage j+2 into buffer (j+2)%3.
+  auto buffer = [&](auto bc) -> T* {
+    constexpr int B = decltype(bc)::value;
+    return B == 0 ? s_x0 : (B == 1 ? s_x1 : s_x2);
   };
-  auto issue_next = [&](int phase, int j, auto bc) {
-    const NextStage ns = next_stage(phase, j, H, Hp, 2);
-    issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<1 - decltype(bc)::value>{});
+  auto issue = [&](int phase, int h, bool on, auto bc) {
+    issue_tile<T, D, R, NW>(buffer(bc), phase == 0 ? v : k, span0, a.T, H, h, on);
+  };
+  auto issue_ahead = [&](int phase, int j, auto bc) {
+    const NextStage ns = stage_after_next(phase, j, H, Hp, 2);
+    issue(ns.phase, ns.head >= 0 ? ns.head : 0, ns.head >= 0, Buf<(decltype(bc)::value + 2) % 3>{});
   };
 
   issue(0, 0, true, Buf<0>{});
@@ -331,7 +366,11 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
         pw[h][b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
             pblk + (size_t)(h < H ? h : 0) * kBandWords + b * 256 + n * 16 + 4 * g));
   }
-  wait_dma();
+  // CW[t] and CS[t] of the tile's queries (rows past T read as zero)
+  issue_scalars<kCompFloats, NW>(s_cw, a.cw, 1, 0, q0 * H * H, a.T * H * H, 1, 0);
+  issue_scalars<kCompFloats, NW>(s_cs, a.cs, 1, 0, q0 * H * H, a.T * H * H, 1, 0);
+  issue(0, 1, 1 < H, Buf<1>{});
+  wait_dma_except<NIW>();
 
   uint32_t mbits = 0;
   {
@@ -347,106 +386,90 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
       }
   }
 
-  // dR_h of every head (then dP_h', then dZ_h, in place)
-  f32x4 dr[HM][kKeyBlocks];
+  // P of every head (heads past H hold 0), and dP_h' = sum_h CW[t,h,h'] dR_h
+  // accumulated head by head over the V phase (then dZ_h' in place)
+  f32x4 pv[HM][kKeyBlocks], dp[HM][kKeyBlocks];
 #pragma unroll
   for (int h = 0; h < HM; ++h)
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) dr[h][b] = zero4();
+    for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[h][b][i] = h < H ? __uint_as_float(pw[h][b][i]) : 0.f;
+        dp[h][b][i] = 0.f;
+      }
+  const float* cw_row = s_cw + (16 * w + n) * H * H;
 
-  // ---- phase 0 (V_h staged): dR_h = dO_h V_h^T, unrolled over the heads ----
-  auto vstage = [&](auto jc, auto bc) __attribute__((always_inline)) {
+  // ---- phase 0 (V_h staged): dR_h = dO_h V_h^T, unrolled over the heads;
+  // each dR_h is mixed as soon as it is complete, while the next tiles stream
+  // in: dCW[t,h,h'] = <dR_h, P_h'>_t and dP_h' += CW[t,h,h'] dR_h ----
+  static_for<0, HM3>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    constexpr int B = decltype(bc)::value;
+    constexpr int F = j % 2;  // dO fragment slot
     if (j >= Hp) return;
-    const T* cur = B == 0 ? s_x0 : s_x1;
-    wait_dma();
-    if (j + 1 < H) load_row_frag<T, D>(fb[1 - B], dO + ((size_t)tc * H + j + 1) * D, g);
+    const T* cur = buffer(Buf<j % 3>{});
+    wait_dma_except<NIW>();
+    if (j + 1 < H) load_row_frag<T, D>(fb[1 - F], dO + ((size_t)tc * H + j + 1) * D, g);
     __builtin_amdgcn_sched_barrier(0);
-    issue_next(0, j, bc);
-    if (j >= H) return;
-    __builtin_amdgcn_s_setprio(2);
+    issue_ahead(0, j, Buf<j % 3>{});
+    if constexpr (j < HM) {  // (stages past HM are padding)
+      if (j >= H) return;
+      f32x4 dr[kKeyBlocks];
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) dr[j][b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, fb[B]);
-    __builtin_amdgcn_s_setprio(0);
-  };
-  static_for<0, HMp / 2>([&](auto pc) {
-    constexpr int j0 = 2 * decltype(pc)::value;
-    vstage(std::integral_constant<int, j0>{}, Buf<0>{});
-    vstage(std::integral_constant<int, j0 + 1>{}, Buf<1>{});
-  });
-
-  // K phase operands of the first head, in flight during the mixing
-  float csb[2][HM];
-  auto load_cs = [&](float (&dst)[HM], int hs) {
-#pragma unroll
-    for (int h = 0; h < HM; ++h) dst[h] = h < H ? comp_at(a.cs, tc, H, h, hs) : 0.f;
-  };
-  load_row_frag<T, D>(fb[0], q + (size_t)tc * H * D, g);
-  load_cs(csb[0], 0);
-
-  // ---- mixing: dCW = dR P^T, dP = CW^T dR, dZ = P (dP - rowsum(dP P)) ----
-  {
-    // P of every head, decoded in place (heads past H hold 0)
-    f32x4 pv[HM][kKeyBlocks];
-#pragma unroll
-    for (int h = 0; h < HM; ++h)
-#pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t u = pw[h][b][i];
-          pv[h][b][i] = h < H ? band_decode<T>(u) : 0.f;
-        }
-    // dCW[t,h,h'] = sum_s dR_h P_h'
-#pragma unroll
-    for (int h = 0; h < HM; ++h)
+      for (int b = 0; b < kKeyBlocks; ++b) dr[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, fb[F]);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int h2 = 0; h2 < HM; ++h2) {
         float x = 0.f;
 #pragma unroll
         for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x = fmaf(dr[h][b][i], pv[h2][b][i], x);
+          for (int i = 0; i < 4; ++i) x = fmaf(dr[b][i], pv[h2][b][i], x);
         x = wave_sum4(x);
-        if (tval && g == 0 && h < H && h2 < H) a.dcw[((size_t)t * H + h) * H + h2] = x;
+        if (tval && g == 0 && h2 < H) a.dcw[((size_t)t * H + j) * H + h2] = x;
       }
-    // dP_h' = sum_h CW[t,h,h'] dR_h (in place), and rowsum(dP_h' P_h')
-    float cwr[HM][HM];
 #pragma unroll
-    for (int h = 0; h < HM; ++h)
+      for (int h2 = 0; h2 < HM; ++h2) {
+        const float c = cw_row[j * H + (h2 < H ? h2 : 0)];
+        const float cj = h2 < H ? c : 0.f;
 #pragma unroll
-      for (int h2 = 0; h2 < HM; ++h2) cwr[h][h2] = (h < H && h2 < H) ? comp_at(a.cw, tc, H, h, h2) : 0.f;
-    float dlt[HM];
+        for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-    for (int h = 0; h < HM; ++h) dlt[h] = 0.f;
+          for (int i = 0; i < 4; ++i) dp[h2][b][i] = fmaf(cj, dr[b][i], dp[h2][b][i]);
+      }
+    }
+  });
+
+  // K phase operands: stage j of the K phase uses slot j%3 and loads slot
+  // (j+1)%3.  Column hs of CS[t] comes from LDS.
+  RowFrag<T, D> qf[3];
+  float csb[3][HM];
+  const float* cs_row = s_cs + (16 * w + n) * H * H;
+  auto load_cs = [&](float (&dst)[HM], int hs) {
+#pragma unroll
+    for (int h = 0; h < HM; ++h) {
+      const float x = cs_row[(h < H ? h : 0) * H + hs];
+      dst[h] = h < H ? x : 0.f;
+    }
+  };
+  load_row_frag<T, D>(qf[0], q + (size_t)tc * H * D, g);
+  load_cs(csb[0], 0);
+
+  // ---- dZ_h = P_h (dP_h - rowsum(dP_h P_h)), in place of dP ----
+  f32x4 (&dr)[HM][kKeyBlocks] = dp;
+#pragma unroll
+  for (int h = 0; h < HM; ++h) {
+    float dl = 0.f;
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float dp[HM];
+      for (int i = 0; i < 4; ++i) dl = fmaf(dp[h][b][i], pv[h][b][i], dl);
+    dl = wave_sum4(dl);
 #pragma unroll
-        for (int h2 = 0; h2 < HM; ++h2) {
-          float x = 0.f;
+    for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-          for (int h = 0; h < HM; ++h) x = fmaf(cwr[h][h2], dr[h][b][i], x);
-          dp[h2] = x;
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < HM; ++h2) {
-          dr[h2][b][i] = dp[h2];
-          dlt[h2] = fmaf(dp[h2], pv[h2][b][i], dlt[h2]);
-        }
-      }
-    // dZ_h = P_h (dP_h - rowsum(dP_h P_h))
-#pragma unroll
-    for (int h = 0; h < HM; ++h) {
-      const float dl = wave_sum4(dlt[h]);
-#pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dr[h][b][i] = pv[h][b][i] * (dr[h][b][i] - dl);
-    }
+      for (int i = 0; i < 4; ++i) dp[h][b][i] = pv[h][b][i] * (dp[h][b][i] - dl);
   }
 
   // ---- phase 1 (K_h' staged): S_h', dCS[.,h'], dS_h', dQ_h' ----
@@ -460,16 +483,17 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
     store_row<T, D>(pending(), pend, g, n);
     pend_h = -1;
   };
-  for_stage_pairs(Hp, [&](int j, auto bc) {
+  for_stage_triples(Hp, [&](int j, auto bc) {
     constexpr int B = decltype(bc)::value;
-    const T* cur = B == 0 ? s_x0 : s_x1;
-    wait_dma();
+    constexpr int B1 = (B + 1) % 3;
+    const T* cur = buffer(bc);
+    wait_dma_except<NIW>();
     const bool real = j < H;
     const int hn = j + 1 < H ? j + 1 : 0;
-    load_row_frag<T, D>(fb[1 - B], q + ((size_t)tc * H + hn) * D, g);
-    load_cs(csb[1 - B], hn);
+    load_row_frag<T, D>(qf[B1], q + ((size_t)tc * H + hn) * D, g);
+    load_cs(csb[B1], hn);
     __builtin_amdgcn_sched_barrier(0);
-    issue_next(1, j, bc);
+    issue_ahead(1, j, bc);
     if (!real) {
       flush();
       return;
@@ -478,7 +502,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
     __builtin_amdgcn_s_setprio(2);
     f32x4 sv[kKeyBlocks];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) sv[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, fb[B]);
+    for (int b = 0; b < kKeyBlocks; ++b) sv[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf[B]);
     __builtin_amdgcn_s_setprio(0);
     // dCS[t,h,j] = sum_s dZ_h S_j (S_j = scale x the contraction)
     static_for<0, HM>([&](auto hc) {
@@ -503,7 +527,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
         for (int h = 0; h < HM; ++h) x = fmaf(csb[B][h], dr[h][b][i], x);
         sv[b][i] = x;
       }
-    if (wval) write_band<T, false>(a.dsband + ((size_t)qb * H + j) * kBandWords, sv, xp, g, n);
+    if (wval) write_band<T>(a.dsband + ((size_t)qb * H + j) * kBandWords, sv, xp, g, n);
     BandOperand<T> dso;
     dso.set(sv);
     __builtin_amdgcn_s_setprio(2);
@@ -591,14 +615,13 @@ __global__ __launch_bounds__(NW * kWave) void dcmha_bwd_kv_kernel(const DcBwdArg
   auto pending = [&](float* dst, float scale) {
     return pending_rows<D>(dst, k0 + 16 * w, n, a.T, H, pend_h >= 0 ? pend_h : 0, pend_h >= 0, scale, xp);
   };
-  // the band operand of a stage: decoded, 0 outside the window
-  auto operand = [&](const u32x4 (&u)[kKeyBlocks], bool enc, BandOperand<T>& op) {
+  // the band operand of a stage: fp32 words, 0 outside the window
+  auto operand = [&](const u32x4 (&u)[kKeyBlocks], BandOperand<T>& op) {
     f32x4 x[kKeyBlocks];
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        x[b][i] = keep_admitted(mbits, b, i, enc ? band_decode<T>(u[b][i]) : __uint_as_float(u[b][i]), 0.f);
+      for (int i = 0; i < 4; ++i) x[b][i] = keep_admitted(mbits, b, i, __uint_as_float(u[b][i]), 0.f);
     op.set(x);
   };
 
@@ -620,7 +643,7 @@ __global__ __launch_bounds__(NW * kWave) void dcmha_bwd_kv_kernel(const DcBwdArg
       return;
     }
     BandOperand<T> op;
-    operand(rb[B], true, op);
+    operand(rb[B], op);
     __builtin_amdgcn_s_setprio(2);
     mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n, pending(a.dv, 1.f));
     __builtin_amdgcn_s_setprio(0);
@@ -645,7 +668,7 @@ __global__ __launch_bounds__(NW * kWave) void dcmha_bwd_kv_kernel(const DcBwdArg
       return;
     }
     BandOperand<T> op;
-    operand(rb[B], false, op);
+    operand(rb[B], op);
     __builtin_amdgcn_s_setprio(2);
     mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n, prev);
     __builtin_amdgcn_s_setprio(0);

@@ -354,6 +354,21 @@ __device__ __forceinline__ void wait_dma() {
   __syncthreads();
 }
 
+// Wait until at most N of this wave's vector-memory operations are in flight
+// and all its LDS operations are done, then barrier.  Loads complete in issue
+// order, so when at least N loads were issued after the operations that must
+// be complete (the DMA of the following stage, say), those are complete after
+// the wait, whatever stores are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_dma_except() {
+  static_assert(N >= 0 && N < 64, "the vector-memory counter holds 6 bits");
+  // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4] (7: no wait), lgkmcnt[11:8]
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // MFMA building blocks over staged tiles
 // ---------------------------------------------------------------------------

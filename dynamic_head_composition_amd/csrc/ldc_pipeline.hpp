@@ -44,6 +44,33 @@ __device__ __forceinline__ NextStage next_stage(int phase, int j, int H, int Hp,
   return {np, nj};
 }
 
+// Three-buffer variant, for kernels that run one workgroup per CU: stage j
+// computes from LDS buffer j%3 while the DMAs of stages j+1 and j+2 are in
+// flight, so every tile gets two stages of lead instead of one.  Phases run
+// over a multiple of three stages (trailing empty stages when 3 does not
+// divide H); body(j, Buf<j%3>).
+template <typename F>
+__device__ __forceinline__ void for_stage_triples(int Hp, F&& body) {
+  for (int j = 0; j < Hp; j += 3) {
+    body(j, Buf<0>{});
+    body(j + 1, Buf<1>{});
+    body(j + 2, Buf<2>{});
+  }
+}
+
+// The stage two after stage j of phase `phase`, in the padded order of
+// for_stage_triples (Hp >= 3), with the conventions of next_stage.  Every
+// stage issues exactly one such DMA (zero bytes when head < 0).
+__device__ __forceinline__ NextStage stage_after_next(int phase, int j, int H, int Hp, int nphases) {
+  int np = phase, nj = j + 2;
+  if (nj >= Hp) {
+    np = phase + 1;
+    nj -= Hp;
+  }
+  if (np >= nphases || nj >= H) return {np, -1};
+  return {np, nj};
+}
+
 // The next stage's DMA is issued in kIssueParts parts spread over the
 // current stage: a wave that issues its whole share right after the barrier
 // can wait thousands of cycles for the memory pipeline to take it while its
