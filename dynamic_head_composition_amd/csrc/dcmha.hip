@@ -199,8 +199,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
     if (!real) return;
     __builtin_amdgcn_s_setprio(2);
     f32x4 s[kKeyBlocks];
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) s[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qfb[B]);
+    mma_dcontract_band<T, D, kKeyBlocks>(s, cur, brow, lo, qfb[B]);
     __builtin_amdgcn_s_setprio(0);
     static_for<0, HM>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
@@ -288,7 +287,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
       BandOperand<T> op;
       op.set(r);
       __builtin_amdgcn_s_setprio(2);
-      mma_tcontract<T, D>(pend, cur, brow, lo, op, g, n, pending());
+      mma_tcontract_pipe<T, D>(pend, cur, brow, lo, op, g, n, pending());
       __builtin_amdgcn_s_setprio(0);
       pend_h = j;
     }
@@ -416,8 +415,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
       if (j >= H) return;
       f32x4 dr[kKeyBlocks];
       __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b) dr[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, fb[F]);
+      mma_dcontract_band<T, D, kKeyBlocks, 1>(dr, cur, brow, lo, fb[F]);
       __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int h2 = 0; h2 < HM; ++h2) {
@@ -501,8 +499,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
     const PendingRow prev = pending();
     __builtin_amdgcn_s_setprio(2);
     f32x4 sv[kKeyBlocks];
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) sv[b] = mma_dcontract<T, D>(zero4(), cur, brow + 16 * b, lo, qf[B]);
+    mma_dcontract_band<T, D, kKeyBlocks>(sv, cur, brow, lo, qf[B]);
     __builtin_amdgcn_s_setprio(0);
     // dCS[t,h,j] = sum_s dZ_h S_j (S_j = scale x the contraction)
     static_for<0, HM>([&](auto hc) {
@@ -531,7 +528,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_bwd_q_kernel(const DcBwdA
     BandOperand<T> dso;
     dso.set(sv);
     __builtin_amdgcn_s_setprio(2);
-    mma_tcontract<T, D>(pend, cur, brow, lo, dso, g, n, prev);
+    mma_tcontract_pipe<T, D>(pend, cur, brow, lo, dso, g, n, prev);
     __builtin_amdgcn_s_setprio(0);
     pend_h = j;
   });

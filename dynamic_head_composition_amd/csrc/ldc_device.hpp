@@ -460,6 +460,50 @@ __device__ __forceinline__ f32x4 mma_dcontract(f32x4 acc, const T* tile, int row
   return acc;
 }
 
+// All NB key blocks of a band at once: s[b] = A x B with the A operand rows
+// row16 + 16b + n.  For bf16 tiles the LDS reads of the next G blocks are
+// issued ahead of the MFMAs of the current G (scheduling groups pin that
+// order), whose G dependent chains alternate: a wave that is alone on its
+// SIMD would otherwise wait out the LDS latency before every MFMA.  G = 2
+// keeps up to 4 blocks of operands in registers, G = 1 up to 2.
+template <typename T, int D, int NB, int G = 2>
+__device__ __forceinline__ void mma_dcontract_band(f32x4 (&s)[NB], const T* tile, int row16,
+                                                   const LaneOffsets<T, D>& lo, const RowFrag<T, D>& f) {
+  if constexpr (Elem<T>::bf16 && !kNarrow<T, D> && NB % G == 0) {
+    using TL = Tile<T, D>;
+    constexpr int KK = D / 32;
+    const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
+    bf16x8 u[NB][KK];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        u[b][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(base + 16 * b * TL::row_bytes +
+                                                                              lo.dk[kk]));
+#pragma unroll
+    for (int b = 0; b < NB; b += G) {
+      f32x4 a[G];
+#pragma unroll
+      for (int c = 0; c < G; ++c) a[c] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int c = 0; c < G; ++c) a[c] = mma(u[b + c][kk], f.v[kk], a[c]);
+#pragma unroll
+      for (int c = 0; c < G; ++c) s[b + c] = a[c];
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, G * KK, 0);  // LDS reads, first G blocks
+#pragma unroll
+    for (int b = 0; b < NB; b += G) {
+      if (b + G < NB) __builtin_amdgcn_sched_group_barrier(0x100, G * KK, 0);  // reads, next G
+      __builtin_amdgcn_sched_group_barrier(0x008, G * KK, 0);                  // MFMAs, these G
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) s[b] = mma_dcontract<T, D>(zero4(), tile, row16 + 16 * b, lo, f);
+  }
+}
+
 // Token-contraction operand: a 16 x 16NB band held in accumulator layout
 // (lane: token rows 4g+i of block b, column n) packed as B-operand k-chunks.
 // bf16: chunk ks covers blocks 2ks, 2ks+1; slot j <-> block 2ks + j/4, row 4g + j%4.
@@ -693,6 +737,63 @@ __device__ __forceinline__ void mma_tcontract(f32x4 (&acc)[D / 16], const T* til
         }
       }
     }
+  }
+}
+
+// mma_tcontract for waves that run alone on their SIMD (bf16, D >= 64): the
+// pending rows are stored first (all column groups), then the LDS operands of
+// column group p+1 are read while the MFMAs of group p run, with the group's
+// two chains (e = 0, 1) alternating, so the LDS latency and the MFMA
+// dependency are paid once per group rather than once per MFMA.
+template <typename T, int D, int NB = kKeyBlocks>
+__device__ __forceinline__ void mma_tcontract_pipe(f32x4 (&acc)[D / 16], const T* tile, int row16,
+                                                   const LaneOffsets<T, D>& lo, const BandOperand<T, NB>& P,
+                                                   int g, int n, const PendingRow& prev) {
+  if constexpr (Elem<T>::bf16 && !kNarrow<T, D>) {
+    using TL = Tile<T, D>;
+    typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+    constexpr int NP = D / 32;
+    const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
+    if (prev.nrows > 0)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) store_slice(prev, acc[2 * p], acc[2 * p + 1], p, g, n);
+    store_fence();
+    bf16x8 a[NP][NB / 2][2];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int ks = 0; ks < NB / 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          // rows 32ks + 4g + n/4 and 16 further down; e flips the lane's 8-byte half
+          const char* a1 = base + (lo.tr[p] ^ (8 * e)) + 32 * ks * TL::row_bytes;
+          const bf16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
+          const bf16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1 + 16 * TL::row_bytes));
+          a[p][ks][e] = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      f32x4 c0 = zero4(), c1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NB / 2; ++ks) {
+        c0 = mma(a[p][ks][0], P.hi[ks], c0);
+        c1 = mma(a[p][ks][1], P.hi[ks], c1);
+        c0 = mma(a[p][ks][0], P.lo[ks], c0);
+        c1 = mma(a[p][ks][1], P.lo[ks], c1);
+      }
+      acc[2 * p] = c0;
+      acc[2 * p + 1] = c1;
+    }
+    constexpr int RD = 2 * NB;  // LDS reads per column group
+    constexpr int MF = 2 * NB;  // MFMAs per column group
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (p + 1 < NP) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+    }
+  } else {
+    mma_tcontract<T, D, NB>(acc, tile, row16, lo, P, g, n, prev);
   }
 }
 
