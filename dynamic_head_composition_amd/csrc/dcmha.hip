@@ -201,22 +201,23 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
     f32x4 s[kKeyBlocks];
     mma_dcontract_band<T, D, kKeyBlocks>(s, cur, brow, lo, qfb[B]);
     __builtin_amdgcn_s_setprio(0);
+    // every slot h < HM, with no branch on H: past H the coefficient is 0
     static_for<0, HM>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
-      if (h < H) {
-        const float c = csb[B][h];
+      const float c = csb[B][h];
 #pragma unroll
-        for (int b = 0; b < kKeyBlocks; ++b)
+      for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) z[h][b][i] = fmaf(c, s[b][i], z[h][b][i]);
-      }
+        for (int i = 0; i < 4; ++i) z[h][b][i] = fmaf(c, s[b][i], z[h][b][i]);
     });
   });
 
-  // ---- softmax of every target head over the window ----
+  // ---- softmax of every target head over the window (every slot h < HM,
+  // with no branch on H, so the heads' reductions can overlap; slots past H
+  // hold finite values and are not stored) ----
   static_for<0, HM>([&](auto hc) {
     constexpr int h = decltype(hc)::value;
-    if (h < H) {
+    {
       float mx = -INFINITY;
 #pragma unroll
       for (int b = 0; b < kKeyBlocks; ++b)
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
       const float inv = sum > 0.f ? 1.f / sum : 0.f;
 #pragma unroll
       for (int b = 0; b < kKeyBlocks; ++b) z[h][b] *= inv;
-      if (save && wval) {  // query-major P band: 16 bytes per lane and key block
+      if (save && wval && h < H) {  // query-major P band: 16 bytes per lane and key block
         uint32_t* blk = a.pband + ((size_t)qb * H + h) * kBandWords;
 #pragma unroll
         for (int b = 0; b < kKeyBlocks; ++b)
@@ -272,15 +273,13 @@ __global__ __launch_bounds__(NW * kWave, 1) void dcmha_fwd_kernel(const DcFwdArg
     f32x4 r[kKeyBlocks];
 #pragma unroll
     for (int b = 0; b < kKeyBlocks; ++b) r[b] = zero4();
-    static_for<0, HM>([&](auto hc) {
+    static_for<0, HM>([&](auto hc) {  // (past H the coefficient is 0)
       constexpr int h = decltype(hc)::value;
-      if (h < H) {
-        const float c = cwb[B][h];
+      const float c = cwb[B][h];
 #pragma unroll
-        for (int b = 0; b < kKeyBlocks; ++b)
+      for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) r[b][i] = fmaf(c, z[h][b][i], r[b][i]);
-      }
+        for (int i = 0; i < 4; ++i) r[b][i] = fmaf(c, z[h][b][i], r[b][i]);
     });
     if (save && wval) write_band<T>(a.rband + ((size_t)qb * H + j) * kBandWords, r, xp, g, n);
     if constexpr (OUT) {
