@@ -8,10 +8,11 @@
 // skinny product x [T, dm] x W [dm, 2H] with 2H <= 16 output columns; the
 // work is bound by reading x (forward) and by reading x and writing dx
 // (backward).
-//  * cg_fwd: MFMA.  Each wave computes a 16-token x 16-column tile, D^T =
+//  * cg_fwd: MFMA.  Each wave computes 16-token x 16-column tiles, D^T =
 //    W^T x^T: the A operand is W^T, staged once per workgroup in LDS (rows
 //    padded by 16 bytes, so the 16 lanes of a group read 16 different banks),
-//    the B operand is x, 16 bytes per lane per k-step straight from HBM.
+//    the B operand is x, 16 bytes per lane per k-step straight from HBM, with
+//    two batches of eight k-steps in flight ahead of the one contracted.
 //  * cg_bwd: VALU streaming.  A thread owns four feature columns i of W (its
 //    4 x 2H weights in registers) and walks a run of tokens: dx[t, i] =
 //    sum_j dCG[t, j] W[i, j] is written as it goes and dW[i, j] += x[t, i]
@@ -32,9 +33,14 @@ constexpr int kCgChunk = 256;    // tokens per cg_bwd workgroup
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <typename T>
+// BPB > 0: dm = BPB x 256 (bf16) or BPB x 128 (fp32), every batch of eight
+// k-steps whole; waves with all kCgBlocks blocks then run a fully unrolled
+// stream of batches with no branch.  BPB = 0: any dm (a multiple of 64).
+template <typename T, int BPB>
 __global__ __launch_bounds__(kCgWaves * kWave) void cg_fwd_kernel(const CgArgs a) {
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int KS = 4 * EPC;               // features per k-step (the 4 groups' chunks): 32 bf16, 16 f32
+  constexpr int U = 8;                      // k-steps per batch of loads
   extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
   T* s_wt = reinterpret_cast<T*>(s_raw);   // W^T [16][dm + EPC]
   const int dm = a.dm, H = a.H, ld = dm + EPC;
@@ -42,53 +48,77 @@ __global__ __launch_bounds__(kCgWaves * kWave) void cg_fwd_kernel(const CgArgs a
   const T* __restrict__ wc = static_cast<const T*>(a.wc);
   const T* __restrict__ wg = static_cast<const T*>(a.wg);
 
-  // stage W^T: row j < H from WC, H <= j < 2H from WG, the rest zero
-  for (int e = threadIdx.x; e < kCgCols * dm; e += blockDim.x) {
-    const int j = e / dm, i = e - j * dm;
-    T val;
-    if (j < H)
-      val = wc[(size_t)i * H + j];
-    else if (j < 2 * H)
-      val = wg[(size_t)i * H + (j - H)];
-    else
-      val = T(0);
-    s_wt[j * ld + i] = val;
-  }
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, n = lane & 15;
-  const T* arow = s_wt + n * ld;  // A operand row: output column n
-  for (int blk = 0; blk < kCgBlocks; ++blk) {
-    const int t0 = ((blockIdx.x * kCgWaves + w) * kCgBlocks + blk) * 16;
-    if (t0 >= a.T) break;  // wave-uniform
-    const int t = t0 + n;
-    const T* xrow = x + (size_t)(t < a.T ? t : a.T - 1) * dm;
-    f32x4 acc = zero4();
-    // k-steps of 32 (bf16) or 16 (f32, one 16-byte chunk = 4 MFMA steps),
-    // eight chunks' loads in flight before their MFMAs
-    constexpr int KS = 4 * EPC;  // features per step (the 4 groups' chunks): 32 bf16, 16 f32
-    for (int k0 = 0; k0 < dm; k0 += 8 * KS) {
-      u32x4 xb[8], wb[8];
+  const int tb0 = (blockIdx.x * kCgWaves + w) * kCgBlocks;  // the wave's first 16-token block
+  const bool full = (tb0 + kCgBlocks) * 16 <= a.T;          // wave-uniform
+  constexpr int NB = kCgBlocks * BPB;                       // batches of a full wave (fast path)
+  constexpr int BP1 = BPB > 0 ? BPB : 1;
+  auto load = [&](u32x4 (&dst)[U], int bi) {
+    const int blk = bi / BP1, k0 = (bi % BP1) * U * KS;
+    const T* xrow = x + (size_t)((tb0 + blk) * 16 + n) * dm + k0 + g * EPC;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u * KS + g * EPC;
-        const bool in = k0 + u * KS < dm;
-        xb[u] = in ? *reinterpret_cast<const u32x4*>(xrow + k) : u32x4{0, 0, 0, 0};
-        wb[u] = in ? *reinterpret_cast<const u32x4*>(arow + k) : u32x4{0, 0, 0, 0};
+    for (int u = 0; u < U; ++u) dst[u] = *reinterpret_cast<const u32x4*>(xrow + u * KS);
+  };
+  u32x4 xb[3][U];
+  if constexpr (BPB > 0) {
+    if (full) {  // the first two batches of x arrive while W^T is staged
+      load(xb[0], 0);
+      load(xb[1], 1);
+    }
+  }
+
+  // Stage W^T: row j < H from WC, H <= j < 2H from WG, the rest zero.
+  if constexpr (BPB > 0 && Elem<T>::bf16) {
+    // dm = 256 BPB: thread r stages rows r + 256 q, q < BPB; all its
+    // 16 BPB loads (each from a valid address) go out before any write
+    T v[BPB][kCgCols];
+#pragma unroll
+    for (int q = 0; q < BPB; ++q) {
+      const int i = (int)threadIdx.x + 256 * q;
+#pragma unroll
+      for (int j = 0; j < kCgCols; ++j) {
+        const T* src = j < H ? wc + (size_t)i * H + j : wg + (size_t)i * H + (j < 2 * H ? j - H : 0);
+        v[q][j] = *src;
       }
+    }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if constexpr (Elem<T>::bf16) {
-          acc = mma(__builtin_bit_cast(bf16x8, wb[u]), __builtin_bit_cast(bf16x8, xb[u]), acc);
-        } else {
-          const f32x4 xf = __builtin_bit_cast(f32x4, xb[u]), wf = __builtin_bit_cast(f32x4, wb[u]);
+    for (int q = 0; q < BPB; ++q) {
+      const int i = (int)threadIdx.x + 256 * q;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = mma(wf[e], xf[e], acc);
+      for (int j = 0; j < kCgCols; ++j) s_wt[j * ld + i] = j < 2 * H ? v[q][j] : T(0);
+    }
+  } else {
+    // any dm: a thread's eight elements of a round are loaded (each from a
+    // valid address) before any is written, so their latencies overlap
+    {
+      const int ne = kCgCols * dm;
+      for (int e0 = threadIdx.x; e0 < ne; e0 += 8 * (int)blockDim.x) {
+        T v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * (int)blockDim.x;
+          const int ec = e < ne ? e : 0;
+          const int j = ec / dm, i = ec - j * dm;
+          const T* src = j < H ? wc + (size_t)i * H + j : wg + (size_t)i * H + (j < 2 * H ? j - H : 0);
+          v[u] = *src;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * (int)blockDim.x;
+          if (e < ne) {
+            const int j = e / dm, i = e - j * dm;
+            s_wt[j * ld + i] = j < 2 * H ? v[u] : T(0);
+          }
         }
       }
     }
-    // lane (g, n): columns 4g+i of token t
+  }
+  __syncthreads();
+
+  const T* arow = s_wt + n * ld;  // A operand row: output column n
+  // lane (g, n) holds columns 4g+i of token t
+  auto store_block = [&](const f32x4& acc, int t) {
     if (t < a.T) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -99,6 +129,59 @@ __global__ __launch_bounds__(kCgWaves * kWave) void cg_fwd_kernel(const CgArgs a
           a.g[(size_t)t * H + (j - H)] = acc[i];
       }
     }
+  };
+  auto contract = [&](f32x4& acc, const u32x4& wb, const u32x4& xv) {
+    if constexpr (Elem<T>::bf16) {
+      acc = mma(__builtin_bit_cast(bf16x8, wb), __builtin_bit_cast(bf16x8, xv), acc);
+    } else {
+      const f32x4 xf = __builtin_bit_cast(f32x4, xv), wf = __builtin_bit_cast(f32x4, wb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mma(wf[e], xf[e], acc);
+    }
+  };
+
+  if constexpr (BPB > 0) {
+    if (full) {
+      // The wave's kCgBlocks x BPB batches as one stream, the loads of the
+      // next two batches in flight while one is contracted (three register
+      // slots, all fixed at compile time).
+      f32x4 acc = zero4();
+      static_for<0, NB>([&](auto bc) {
+        constexpr int bi = decltype(bc)::value;
+        if constexpr (bi + 2 < NB) load(xb[(bi + 2) % 3], bi + 2);
+        constexpr int k0 = (bi % BPB) * U * KS;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          contract(acc, *reinterpret_cast<const u32x4*>(arow + k0 + u * KS + g * EPC), xb[bi % 3][u]);
+        if constexpr (bi % BPB == BPB - 1) {
+          store_block(acc, (tb0 + bi / BPB) * 16 + n);
+          acc = zero4();
+        }
+      });
+      return;
+    }
+  }
+  // any dm, and the last waves of the stream: block by block, eight k-steps'
+  // loads in flight before their MFMAs
+  for (int blk = 0; blk < kCgBlocks; ++blk) {
+    const int t0 = (tb0 + blk) * 16;
+    if (t0 >= a.T) break;  // wave-uniform
+    const int t = t0 + n;
+    const T* xrow = x + (size_t)(t < a.T ? t : a.T - 1) * dm;
+    f32x4 acc = zero4();
+    for (int k0 = 0; k0 < dm; k0 += U * KS) {
+      u32x4 xb[U], wb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + u * KS + g * EPC;
+        const bool in = k0 + u * KS < dm;
+        xb[u] = in ? *reinterpret_cast<const u32x4*>(xrow + k) : u32x4{0, 0, 0, 0};
+        wb[u] = in ? *reinterpret_cast<const u32x4*>(arow + k) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) contract(acc, wb[u], xb[u]);
+    }
+    store_block(acc, t);
   }
 }
 
@@ -126,16 +209,26 @@ __global__ __launch_bounds__(kCgThreads) void cg_bwd_kernel(const CgBwdArgs a) {
   const int nf = dm / 4;  // feature threads per sub-group
   const int t0 = blockIdx.x * kCgChunk;
   const int nt = a.T - t0 < kCgChunk ? a.T - t0 : kCgChunk;
-  for (int e = threadIdx.x; e < kCgChunk * kCgCols; e += blockDim.x) {
-    const int tt = e / kCgCols, j = e - tt * kCgCols;
-    float val = 0.f;
-    if (tt < nt) {
-      if (j < H)
-        val = a.dc[(size_t)(t0 + tt) * H + j];
-      else if (j < J)
-        val = a.dg[(size_t)(t0 + tt) * H + (j - H)];
+  // loads unconditional (from a valid address, then selected), so that a
+  // thread's loads are in flight together rather than waited for one by one
+  {
+    constexpr int NE = kCgChunk * kCgCols;
+    constexpr int R = (NE + 511) / 512;  // rounds for the smallest block (512 threads)
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = threadIdx.x + r * (int)blockDim.x;
+      const int tt = e / kCgCols, j = e - tt * kCgCols;
+      const int tc = t0 + (tt < nt ? tt : 0);
+      const float* src = j < H ? a.dc + (size_t)tc * H + j : a.dg + (size_t)tc * H + (j < J ? j - H : 0);
+      v[r] = *src;
     }
-    s_d[e] = val;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = threadIdx.x + r * (int)blockDim.x;
+      const int tt = e / kCgCols, j = e - tt * kCgCols;
+      if (e < NE) s_d[e] = (tt < nt && j < J) ? v[r] : 0.f;
+    }
   }
   __syncthreads();
   const int nsub = blockDim.x / nf;  // token sub-groups
@@ -156,7 +249,9 @@ __global__ __launch_bounds__(kCgThreads) void cg_bwd_kernel(const CgBwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const size_t r = (size_t)(i0 + c) * H;
-      wv[c][j] = j < H ? tof(wc[r + j]) : j < J ? tof(wg[r + j - H]) : 0.f;
+      const T* src = j < H ? wc + r + j : wg + r + (j < J ? j - H : 0);
+      const float wj = tof(*src);
+      wv[c][j] = j < J ? wj : 0.f;
       acc[c][j] = 0.f;
     }
   // this sub-group's tokens: [lo, hi) of the chunk
@@ -257,10 +352,26 @@ hipError_t cg_fwd_dispatch(int dtype, const CgArgs& a, hipStream_t st) {
   const int per_wg = kCgWaves * kCgBlocks * 16;
   const int nblk = (int)((a.T + per_wg - 1) / per_wg);
   const size_t lds = (size_t)kCgCols * (a.dm + (dtype == 0 ? 8 : 4)) * (dtype == 0 ? 2 : 4);
+  auto go = [&](auto tc) {
+    using TT = typename decltype(tc)::type;
+    const int per_batch = 8 * 4 * (16 / (int)sizeof(TT));  // features per batch of eight k-steps
+    const int bpb = a.dm % per_batch == 0 ? a.dm / per_batch : 0;
+    const dim3 grid(nblk), block(kCgWaves * kWave);
+    if (bpb == 1)
+      hipLaunchKernelGGL((cg_fwd_kernel<TT, 1>), grid, block, lds, st, a);
+    else if (bpb == 2)
+      hipLaunchKernelGGL((cg_fwd_kernel<TT, 2>), grid, block, lds, st, a);
+    else if (bpb == 3)
+      hipLaunchKernelGGL((cg_fwd_kernel<TT, 3>), grid, block, lds, st, a);
+    else if (bpb == 4)
+      hipLaunchKernelGGL((cg_fwd_kernel<TT, 4>), grid, block, lds, st, a);
+    else
+      hipLaunchKernelGGL((cg_fwd_kernel<TT, 0>), grid, block, lds, st, a);
+  };
   if (dtype == 0)
-    hipLaunchKernelGGL(cg_fwd_kernel<bf16_t>, dim3(nblk), dim3(kCgWaves * kWave), lds, st, a);
+    go(TypeTag<bf16_t>{});
   else
-    hipLaunchKernelGGL(cg_fwd_kernel<float>, dim3(nblk), dim3(kCgWaves * kWave), lds, st, a);
+    go(TypeTag<float>{});
   return hipGetLastError();
 }
 
