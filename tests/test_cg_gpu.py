@@ -24,6 +24,13 @@ CASES = [  # (T, dm, H, dtype, seed)
     (257, 1024, 8, "bf16", 4),
     (4097, 768, 6, "bf16", 5),
     (33, 64, 2, "bf16", 6),
+    # the forward's unrolled paths (dm = 256, 512 per 8-step batch of bf16,
+    # 128 of fp32) with whole 64-token waves and a ragged last one
+    (640, 256, 4, "bf16", 8),
+    (333, 512, 7, "bf16", 9),
+    (300, 256, 5, "f32", 10),
+    (129, 384, 2, "f32", 11),
+    (200, 512, 8, "f32", 12),
 ]
 
 
