@@ -32,6 +32,11 @@ the same GPT-2 small shape, reported in the same format.
 With --workload cg the step is the generator of the layer's weights (C = x WC,
 G = x WG from the 768-wide hidden state) forward and backward.
 
+With --workload fused the step is the attention block's forward with the
+Lightweight DC layer fused into the main attention kernel (ldc_fused_fwd) on
+the GPT-2 small forward workload; the unfused pair (ldc_main_attention_fwd,
+then ldc_fwd) is timed beside it.
+
 With --workload mudd the step is one MUDD mix forward and backward
 (mudd_fwd + mudd_bwd) over a GPT-2 small token stream (65,536 tokens, model
 dim 768, 13 layer streams, 4 ways), reported in the same format.
@@ -404,6 +409,133 @@ def bench_dcmha(args):
     print(json.dumps(line), flush=True)
 
 
+FUSED_METRIC = "attention block fwd tokens/s on 1 MI355X (GPT-2-small shape): main attention + LDC fused"
+FUSED_SOURCES = ("ldc_device.hpp", "ldc_pipeline.hpp", "fused.hip", "fused_internal.h")
+
+
+def fused_cpu_baseline(w, budget_s: float, chunk: int = 512):
+    """Time the fp64 fused-block oracle on leading query slices of the stream
+    (each query with its whole run and window) until `budget_s` seconds."""
+    from oracle import fused_oracle as fo
+    from oracle import ldc_oracle as orc
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.T and time.perf_counter() - t0 < budget_s:
+        lo, hi = done, min(w.T, done + chunk)
+        fo.main_attention(w.q, w.k, w.v, w.doc, w.scale, queries=range(lo, hi))
+        orc.forward_slice(w.q, w.k, w.v, w.c, w.g, w.doc, lo, hi, window=w.window, scale=w.scale)
+        done = hi
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            **host_cpu(),
+            "sample": f"fp64 oracle of the block (main attention of each query over its run + the "
+                      f"Lightweight DC layer) over queries [0, {done}) of the same stream in "
+                      f"{chunk}-query slices; {el:.1f} s"}
+
+
+def bench_fused(args):
+    """The block's attention forward with the Lightweight DC layer fused into
+    the main attention kernel; the unfused pair (main attention alone, then the
+    Lightweight DC forward) timed beside it."""
+    import torch
+    import dynamic_head_composition_amd as ldc
+    from dynamic_head_composition_amd import fused
+    from dynamic_head_composition_amd import workloads as wl
+
+    ldc.load_library()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    log("generating workload 1 ...")
+    w = wl.config_workload(1, T=args.tokens)
+    x = w.torch_inputs("cuda", with_do=False)
+    T, H, d = w.T, w.H, w.d
+    elem = 2 if w.dtype == "bf16" else 4
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o, m, lo_ = (torch.empty((T, H, d), **f32) for _ in range(3))
+    ins = (x["q"], x["k"], x["v"], x["c"], x["g"], x["doc"])
+    code = ldc.LDC_BF16 if w.dtype == "bf16" else ldc.LDC_F32
+    ws = torch.empty(max(16, fused.workspace_bytes(code, T, H, d, w.window)), dtype=torch.uint8, device="cuda")
+    ws_m = torch.empty(max(16, fused.main_workspace_bytes(T)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        fused.fwd(*ins, window=w.window, scale=w.scale, out=o, workspace=ws)
+
+    def unfused(evs):
+        evs[0].record()
+        fused.main_fwd(x["q"], x["k"], x["v"], x["doc"], scale=w.scale, out=m, workspace=ws_m)
+        evs[1].record()
+        ldc.fwd(*ins, window=w.window, scale=w.scale, out=lo_)
+        evs[2].record()
+
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if not bool(torch.isfinite(o).all()):
+        raise SystemExit("non-finite outputs")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    fst = stats_us([e[0].elapsed_time(e[1]) for e in evs])
+    # the unfused pair, for comparison (not part of the step)
+    uevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        unfused(uevs[i])
+    torch.cuda.synchronize()
+    mst = stats_us([e[0].elapsed_time(e[1]) for e in uevs])
+    lst = stats_us([e[1].elapsed_time(e[2]) for e in uevs])
+    ust = stats_us([e[0].elapsed_time(e[2]) for e in uevs])
+
+    main_pairs = valid_pairs(w.doc, T)          # every key of the query's run up to the query
+    ldc_pairs = valid_pairs(w.doc, w.window)
+    # MFMA work per admitted pair and head: the score (2d) and the value
+    # contraction (2d), for the main attention and the Lightweight DC branch
+    flops = 4.0 * H * d * (main_pairs + ldc_pairs)
+    sec = fst["median_us"] * 1e-6
+    achieved = flops / sec / 1e12
+    alg_bytes = spec_bytes_per_token(H, d, elem)["ldc_fwd"] * T  # Q, K, V, C, G, doc in; O out
+    value = T / (ms_per_step * 1e-3)
+    line = {
+        "metric": FUSED_METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "heads": H, "head_dim": d, "window": w.window,
+                   "recipe": w.recipe, "main_pairs": main_pairs, "ldc_pairs": ldc_pairs,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "fused_fwd", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(("fused_fwd",), w.name, FUSED_SOURCES),
+                     "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes,
+                     "hbm_frac": round(alg_bytes / sec / 1e9 / HBM_PEAK_GBPS, 4)},
+        "kernels": {"fused_fwd": fst, "main_attention_fwd": mst, "ldc_fwd": lst},
+        "unfused_us": ust,
+        "fused_speedup_vs_unfused": round(ust["median_us"] / fst["median_us"], 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = fused_cpu_baseline(w, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 CG_METRIC = "C/G generator fwd+bwd tokens/s on 1 MI355X (GPT-2-small hidden state)"
 CG_KERNELS = ("cg_fwd", "cg_bwd")
 CG_SOURCES = ("ldc_device.hpp", "cg.hip", "cg_internal.h")
@@ -604,10 +736,11 @@ def main():
     # (measured: 5 warm-up steps read ~10% below 100); 100 steps take ~50 ms
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = GPT-2 small layer fwd+bwd)")
-    ap.add_argument("--workload", choices=("ldc", "dcmha", "cg", "mudd"), default="ldc",
+    ap.add_argument("--workload", choices=("ldc", "dcmha", "cg", "mudd", "fused"), default="ldc",
                     help="ldc: the Lightweight DC layer (default); dcmha: full DCMHA composition at "
                          "the same shape; cg: the generator of C and G from the hidden state; "
-                         "mudd: MUDD layer mixing")
+                         "mudd: MUDD layer mixing; fused: the block's main attention with the "
+                         "Lightweight DC layer fused in (forward)")
     ap.add_argument("--tokens", type=int, default=None, help="truncate the stream (quick runs only)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -627,6 +760,8 @@ def main():
         return bench_dcmha(args)
     if args.workload == "cg":
         return bench_cg(args)
+    if args.workload == "fused":
+        return bench_fused(args)
 
     import torch
     import dynamic_head_composition_amd as ldc

@@ -78,10 +78,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         getattr(lib, nm).argtypes = [i32, i64, i32, i32, i32]
         getattr(lib, nm).restype = sz
     lib.ldc_cg_fwd.argtypes = [i32, i64, i32, i32] + [vp] * 5 + [vp]
-    lib.ldc_fused_fwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 7 + [vp]
+    lib.ldc_fused_fwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 7 + [vp, sz, vp]
     lib.ldc_fused_fwd.restype = i32
-    lib.ldc_main_attention_fwd.argtypes = [i32, i64, i32, i32, f32] + [vp] * 5 + [vp]
+    lib.ldc_fused_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
+    lib.ldc_fused_fwd_workspace_bytes.restype = sz
+    lib.ldc_main_attention_fwd.argtypes = [i32, i64, i32, i32, f32] + [vp] * 5 + [vp, sz, vp]
     lib.ldc_main_attention_fwd.restype = i32
+    lib.ldc_main_attention_workspace_bytes.argtypes = [i64]
+    lib.ldc_main_attention_workspace_bytes.restype = sz
     lib.ldc_cg_fwd.restype = i32
     lib.ldc_cg_bwd.argtypes = [i32, i64, i32, i32] + [vp] * 8 + [vp, sz, vp]
     lib.ldc_cg_bwd.restype = i32

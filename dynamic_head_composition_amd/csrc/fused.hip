@@ -1,5 +1,5 @@
-// The Lightweight DC layer fused with the attention block's main attention,
-// forward, for gfx950.
+// The attention block's main attention with the Lightweight DC layer fused
+// in, forward, for gfx950.
 //
 // Layer (AITNT page "一个国产AI小透明，连续两次刷新NanoGPT Speedrun世界纪录",
 // section "第二刀-砍层内", Lightweight DC paragraph: the branch reuses the
@@ -9,43 +9,123 @@
 // document ids (keys run_start(t) .. t); the second term: the Lightweight DC
 // layer (its window and document cut, Pbar = sum_h C[t,h] P_h).
 //
-// One workgroup per 64-query tile (4 waves, one per SIMD) walks every head.
-//  * Lightweight DC phase, per head: the window tile of K (keys q0-128 ..
-//    q0+63) gives each wave its 8-block band of scores; the band's softmax
-//    (window and document masks) is composed into Pbar with C[t,h]
-//    (registers, all heads).
-//  * Main pass, per head: 192-key tiles of K, then of V, from the run start of
-//    the tile's first query up to q0-129, then the window tile: flash-style
-//    online softmax (running max and sum per query, an fp32 accumulator of the
-//    wave's 16 rows x d).  The window tile's V contraction takes one band
-//    operand: the main weights plus l G[t,h] Pbar on the wave's band blocks
-//    (l the final running sum), so O = acc / l carries both terms and is
-//    written once.
-// The window tile's K is read twice per head (once per phase); its V once.
-// Tiles stream into LDS by DMA, double-buffered.  Deterministic.
+// Launches (one stream, in order):
+//  1. run_marks / run_starts: run_start(t) of every token (a two-level
+//     prefix maximum of the run boundaries over 1024-token blocks).
+//  2. (fused only) the Lightweight DC score pass: the composed map Pbar of
+//     every 16-query block over its 128-key band, in the layout of the
+//     layer's saved state (it is that state, usable by the backward pass).
+//  3. attn_fwd_kernel: one workgroup of 8 waves per (128-query tile, head),
+//     flash-style: 128-key stages of K then V stream through a four-slot LDS
+//     ring by DMA (three half-stages in flight), scores on MFMA, online
+//     softmax in registers, P V on MFMA into an fp32 accumulator per wave
+//     (16 queries x d).  Stages run from the tile's earliest run start to the
+//     tile's last query; the last two (the keys q0-128 .. q0+127) hold every
+//     key of the tile's Lightweight DC bands, so after the last stage the
+//     band's value contraction l G Pbar V joins the accumulator (l the final
+//     softmax sum) and O = acc / l is written once.
+// Work items are (tile, head) pairs, so a long document's tiles spread over
+// the whole chip; every launch is deterministic.
 #include "fused_internal.h"
 #include "ldc_device.hpp"
-#include "ldc_pipeline.hpp"
 
 namespace ldc {
 
-constexpr int kFNW = 4;                 // waves per workgroup
-constexpr int kFBQ = 16 * kFNW;         // queries per workgroup
-constexpr int kFBlocks = 12;            // 16-row blocks per staged tile
-constexpr int kFRows = 16 * kFBlocks;   // 192 rows per staged tile
-constexpr int kFWin = 128;              // the window tile starts 128 keys before the tile's first query
+// ---------------------------------------------------------------------------
+// Run starts
+// ---------------------------------------------------------------------------
+constexpr int kRunBlock = 1024;  // tokens per run-start block (256 threads x 4)
 
-// acc += X^T P over a staged tile's NB blocks (X the tile's rows, P a band
-// operand in accumulator layout): mma_tcontract_pipe's order (the LDS reads of
-// column group p+1 ahead of the MFMAs of group p, the two chains of a group
-// alternating) with the chains started from acc instead of zero.
-template <typename T, int D, int NB>
-__device__ __forceinline__ void tcontract_acc(f32x4 (&acc)[D / 16], const T* tile, int row16,
-                                              const LaneOffsets<T, D>& lo, const BandOperand<T, NB>& P) {
-  using TL = Tile<T, D>;
+__device__ __forceinline__ int block_max_256(int x, int* red) {
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = x;
+  __syncthreads();
+  const int r = max(max(red[0], red[1]), max(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+// is t the first token of its run (t == 0 or its id differs from t-1's)?
+__device__ __forceinline__ bool run_boundary(const int32_t* __restrict__ doc, int t) {
+  return t == 0 || doc[t] != doc[t - 1];
+}
+
+// last[b]: the last run boundary in tokens [1024 b, 1024 b + 1024), or -1.
+__global__ __launch_bounds__(256) void run_marks_kernel(const int32_t* __restrict__ doc, int T,
+                                                        int* __restrict__ last) {
+  __shared__ int red[4];
+  const int t0 = blockIdx.x * kRunBlock + 4 * threadIdx.x;
+  int best = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (t0 + j < T && run_boundary(doc, t0 + j)) best = t0 + j;
+  best = block_max_256(best, red);
+  if (threadIdx.x == 0) last[blockIdx.x] = best;
+}
+
+// rs[t] = run_start(t): the larger of the last boundary before the block
+// (from the block summaries, looked back 256 blocks at a time; block 0 always
+// holds token 0's boundary) and the block's own prefix maximum up to t.
+__global__ __launch_bounds__(256) void run_starts_kernel(const int32_t* __restrict__ doc, int T,
+                                                         const int* __restrict__ last,
+                                                         int* __restrict__ rs) {
+  __shared__ int red[4];
+  __shared__ int wtot[4];
+  const int b = blockIdx.x;
+  int carry = -1;
+  for (int base = b - 1; base >= 0 && carry < 0; base -= 256) {  // workgroup-uniform
+    const int j = base - (int)threadIdx.x;
+    carry = block_max_256(j >= 0 ? last[j] : -1, red);
+  }
+  const int t0 = b * kRunBlock + 4 * threadIdx.x;
+  int r[4];
+  int run = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (t0 + j < T && run_boundary(doc, t0 + j)) run = t0 + j;
+    r[j] = run;
+  }
+  // exclusive prefix maximum of the threads' last values
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = run;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x = max(x, y);
+  }
+  if (lane == 63) wtot[w] = x;
+  int before = __shfl_up(x, 1);
+  if (lane == 0) before = -1;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) before = max(before, wtot[i]);
+  before = max(before, carry);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (t0 + j < T) rs[t0 + j] = max(before, r[j]);
+}
+
+// ---------------------------------------------------------------------------
+// Main attention
+// ---------------------------------------------------------------------------
+constexpr int kANW = 8;                // waves per workgroup
+constexpr int kABQ = 16 * kANW;        // 128 queries per tile
+constexpr int kARows = 128;            // keys per stage
+constexpr int kABlocks = kARows / 16;  // 8 key blocks per stage
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+// acc += X^T P over NB 16-row blocks of staged tiles, block b starting at LDS
+// byte address blk[b] (X a tile's rows, P a band operand in accumulator
+// layout; HILO: P carried as hi + lo bf16 parts, else hi only).  The LDS
+// transpose reads of column group p+1 are issued ahead of the MFMAs of group
+// p; each group's two chains alternate.
+template <typename T, int D, int NB, bool HILO>
+__device__ __forceinline__ void pv_blocks(f32x4 (&acc)[D / 16], const char* const (&blk)[NB],
+                                          const LaneOffsets<T, D>& lo, const BandOperand<T, NB>& P) {
   typedef __attribute__((address_space(3))) bf16x4 lds_v4;
   constexpr int NP = D / 32;
-  const char* base = reinterpret_cast<const char*>(tile) + row16 * TL::row_bytes;
+  constexpr int PER = HILO ? 4 : 2;  // MFMAs per (p, ks)
   bf16x8 a[NP][NB / 2][2];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
@@ -53,9 +133,9 @@ __device__ __forceinline__ void tcontract_acc(f32x4 (&acc)[D / 16], const T* til
     for (int ks = 0; ks < NB / 2; ++ks)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const char* a1 = base + (lo.tr[p] ^ (8 * e)) + 32 * ks * TL::row_bytes;
-        const bf16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
-        const bf16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1 + 16 * TL::row_bytes));
+        const int off = lo.tr[p] ^ (8 * e);
+        const bf16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(blk[2 * ks] + off));
+        const bf16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(blk[2 * ks + 1] + off));
         a[p][ks][e] = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
@@ -65,8 +145,10 @@ __device__ __forceinline__ void tcontract_acc(f32x4 (&acc)[D / 16], const T* til
     for (int ks = 0; ks < NB / 2; ++ks) {
       c0 = mma(a[p][ks][0], P.hi[ks], c0);
       c1 = mma(a[p][ks][1], P.hi[ks], c1);
-      c0 = mma(a[p][ks][0], P.lo[ks], c0);
-      c1 = mma(a[p][ks][1], P.lo[ks], c1);
+      if constexpr (HILO) {
+        c0 = mma(a[p][ks][0], P.lo[ks], c0);
+        c1 = mma(a[p][ks][1], P.lo[ks], c1);
+      }
     }
     acc[2 * p] = c0;
     acc[2 * p + 1] = c1;
@@ -75,267 +157,235 @@ __device__ __forceinline__ void tcontract_acc(f32x4 (&acc)[D / 16], const T* til
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     if (p + 1 < NP) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NB, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, PER * NB / 2, 0);
   }
 }
 
-// The stage list of a workgroup: kind, head, first tile row.
-//   0: Lightweight DC phase, window tile of K      (heads 0..H-1)
-//   1: main pass, K tile before the window          2: main pass, its V tile
-//   3: main pass, window tile of K                  4: main pass, window tile of V
-//  -1: past the end (no DMA)
-struct FStage {
-  int kind, h, row0;
-};
-
 template <typename T, int D, bool LDC>
-__global__ __launch_bounds__(kFNW * kWave, 1) void fused_fwd_kernel(const FusedArgs a) {
-  constexpr int NW = kFNW, BQ = kFBQ, R = kFRows, NBT = kFBlocks;
-  __shared__ __attribute__((aligned(1024))) T s_x0[R * D];
-  __shared__ __attribute__((aligned(1024))) T s_x1[R * D];
-  __shared__ __attribute__((aligned(16))) int s_doc[(R + 63) / 64 * 64];
+__global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a) {
+  constexpr int NW = kANW, BQ = kABQ, R = kARows, NB = kABlocks;
+  constexpr int NIW = tile_insts_per_wave<T, D, R, NW>();  // DMA instructions per wave per half-stage
+  constexpr int NBAND = LDC ? kKeyBlocks * 4 : 0;          // band loads per lane
+  using TL = Tile<T, D>;
+  // the ring: slot i holds half-stage j with j % 4 == i (K of stage s is
+  // half-stage 2s, V of stage s is 2s + 1).  Four separate arrays, always
+  // chosen at compile time, so that the compiler sees which LDS object a
+  // pending DMA writes and does not wait for it before reading another.
+  __shared__ __attribute__((aligned(1024))) T s_r0[R * D];
+  __shared__ __attribute__((aligned(1024))) T s_r1[R * D];
+  __shared__ __attribute__((aligned(1024))) T s_r2[R * D];
+  __shared__ __attribute__((aligned(1024))) T s_r3[R * D];
   __shared__ __attribute__((aligned(16))) float s_xp[NW * 512];
-  __shared__ int s_red[NW];
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
   const T* __restrict__ v = static_cast<const T*>(a.v);
-
+  const int H = a.H;
+  const int item = blockIdx.x;
+  const int tile = item / H, h = item - tile * H;
+  const int q0 = tile * BQ;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, n = lane & 15;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int q0 = tile * BQ;
-  const int w0 = q0 - kFWin;  // first key of the window tile
   const int t = q0 + 16 * w + n;
-  const bool tval = t < a.T;
-  const int tc = tval ? t : a.T - 1;
-  const int H = a.H;
+  const int tc = t < a.T ? t : a.T - 1;
+  const int tw = q0 + 16 * w;  // the wave's first query
   const float sl2 = a.scale * kLog2e;
-  float* xp = s_xp + w * 512;
   const LaneOffsets<T, D> lo(g, n);
 
-  // ks0: first token of the run holding q0 (the earliest key of the tile's
-  // main attention), found by scanning back 256 ids at a time
-  int ks0 = 0;
-  {
-    const int d0 = a.doc[q0];
-    for (int base = q0 - 1; base >= 0; base -= 256) {  // workgroup-uniform
-      const int s = base - (int)threadIdx.x;
-      const int ds = a.doc[s >= 0 ? s : 0];
-      const uint64_t mm = __ballot(s >= 0 && ds != d0);
-      if (lane == 0) s_red[w] = mm ? base - (64 * w + __builtin_ctzll(mm)) : -1;
-      __syncthreads();
-      int best = -1;
-#pragma unroll
-      for (int i = 0; i < NW; ++i) best = s_red[i] > best ? s_red[i] : best;
-      __syncthreads();
-      if (best >= 0) {
-        ks0 = best + 1;
-        break;
-      }
-    }
-  }
-  const int span = w0 - ks0;  // run keys before the window tile
+  // operands of the whole item (older than every DMA below)
+  RowFrag<T, D> qf;
+  load_row_frag<T, D, true>(qf, q + ((size_t)tc * H + h) * D, g);
+  const int kslo = a.rs[tc];
+  const int ks0 = __builtin_amdgcn_readfirstlane(a.rs[q0]);  // earliest key of the tile
+  float gh = 0.f;
+  if constexpr (LDC) gh = a.g[(size_t)tc * H + h];
+
+  // stages: chunks of R keys from (at or before) ks0 up to q0-129, then
+  // W1 = [q0-128, q0) and W2 = [q0, q0+128)
+  const int w1 = q0 - R;
+  const int span = w1 - ks0;
   const int nc = span > 0 ? (span + R - 1) / R : 0;
-  const int per = 2 * (nc + 1);
-  const int npre = LDC ? H : 0;
-  const int nstages = npre + H * per;
-  auto desc = [&](int G) -> FStage {
-    if (G < npre) return {0, G, w0};
-    G -= npre;
-    if (G >= H * per) return {-1, 0, w0};
-    const int h = G / per, r = G - h * per, c = r >> 1;
-    if (c < nc) return {(r & 1) ? 2 : 1, h, w0 - R * (nc - c)};
-    return {(r & 1) ? 4 : 3, h, w0};
+  auto stage_row = [&](int s) __attribute__((always_inline)) { return w1 - R * (nc - s); };
+  auto slot = [&](auto c) __attribute__((always_inline)) -> T* {
+    constexpr int I = decltype(c)::value & 3;
+    return I == 0 ? s_r0 : I == 1 ? s_r1 : I == 2 ? s_r2 : s_r3;
   };
-  auto buffer = [&](auto bc) -> T* { return decltype(bc)::value == 0 ? s_x0 : s_x1; };
-  auto issue_stage = [&](int G, auto bc) {
-    const FStage st = desc(G);
-    const bool on = st.kind >= 0;
-    issue_tile<T, D, R, NW>(buffer(bc), (st.kind == 2 || st.kind == 4) ? v : k, st.row0, a.T, H, on ? st.h : 0,
-                            on);
+  // DMA of half-stage j (j % 4 == I) into its slot
+  auto issue_half = [&](auto c, int j) __attribute__((always_inline)) {
+    issue_tile<T, D, R, NW>(slot(c), (decltype(c)::value & 1) ? v : k, stage_row(j >> 1), a.T, H, h);
   };
-  // a stage's per-head operands, loaded one stage ahead (unconditionally)
-  RowFrag<T, D> qf[2];
-  float cc[2] = {0.f, 0.f}, gg[2] = {0.f, 0.f};
-  auto load_ops = [&](int G, auto sc) {
-    constexpr int S = decltype(sc)::value;
-    const FStage st = desc(G);
-    const int hh = st.kind >= 0 ? st.h : 0;
-    load_row_frag<T, D, true>(qf[S], q + ((size_t)tc * H + hh) * D, g);
-    if constexpr (LDC) {  // (no C or G without the Lightweight DC terms)
-      cc[S] = a.c[(size_t)tc * H + hh];
-      gg[S] = a.g[(size_t)tc * H + hh];
-    }
-  };
+  issue_half(IC<0>{}, 0);
+  issue_half(IC<1>{}, 1);
+  issue_half(IC<2>{}, 2);
+  // the item's operand loads (older) are complete, the DMA still in flight;
+  // said here, the compiler need not drain the DMA before the stage loop
+  __builtin_amdgcn_s_waitcnt(((3 * NIW) & 15) | (((3 * NIW) >> 4) << 14) | (7 << 4) | (15 << 8));
 
-  issue_stage(0, Buf<0>{});
-  issue_doc<R, NW>(s_doc, a.doc, w0, a.T);
-  load_ops(0, Buf<0>{});
-  wait_dma();
+  // a stage needs masking when it holds keys below the wave's latest run
+  // start (run starts never decrease, so that of its last query) or past
+  // the wave's first query
+  const int kmax = __builtin_amdgcn_readfirstlane(a.rs[tw + 15 < a.T ? tw + 15 : a.T - 1]);
 
-  // per-query run start: ks0, or the last run boundary in (q0, t]
-  int kslo = ks0;
-  for (int s = q0 + 1; s <= t && s < a.T; ++s)
-    if (s_doc[s - w0] != s_doc[s - 1 - w0]) kslo = s;
-  // admission bits of the Lightweight DC band (bit 4b+i: key q0-112+16w+16b+4g+i)
-  uint32_t mbits = 0;
-  if constexpr (LDC) {
-    const int dt = s_doc[t - w0];
-#pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 + 16 * w + 16 * b + 4 * g + i;
-        const int s = w0 + r;
-        const bool ok = tval & (s >= 0) & (s <= t) & (t - s < a.window) & (s_doc[r] == dt);
-        mbits |= (ok ? 1u : 0u) << (4 * b + i);
-      }
-  }
-
-  f32x4 pbar[kKeyBlocks], pw[NBT], acc[D / 16];
-#pragma unroll
-  for (int b = 0; b < kKeyBlocks; ++b) pbar[b] = zero4();
-#pragma unroll
-  for (int b = 0; b < NBT; ++b) pw[b] = zero4();
+  f32x4 acc[D / 16];
 #pragma unroll
   for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
   float m = -1e30f, l = 0.f;  // running max (log2 units; finite start) and sum
+  BandOperand<T, NB> pop;     // the current stage's P (its hi part is used)
 
-  // online softmax over a scored tile (key of entry (b, i): row0 + 16b + 4g + i)
-  auto online = [&](const f32x4 (&s)[NBT], int row0, bool window) {
-    float z[NBT][4];
+  // scores of a K stage and the online-softmax update; leaves P in pop
+  auto k_stage = [&](const T* kt, int row0) __attribute__((always_inline)) {
+    f32x4 s[NB];
+    __builtin_amdgcn_s_setprio(1);
+    mma_dcontract_band<T, D, NB>(s, kt, 0, lo, qf);
+    __builtin_amdgcn_s_setprio(0);
     float mx = -INFINITY;
+    if (row0 < kmax || row0 + R - 1 > tw) {  // wave-uniform
 #pragma unroll
-    for (int b = 0; b < NBT; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = row0 + 16 * b + 4 * g + i;
-        const bool ok = (key >= kslo) & (!window | (key <= t));
-        z[b][i] = ok ? s[b][i] * sl2 : -INFINITY;
-        mx = fmaxf(mx, z[b][i]);
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int key = row0 + 16 * b + 4 * g + i;
+          s[b][i] = (key >= kslo && key <= t) ? s[b][i] * sl2 : -INFINITY;
+          mx = fmaxf(mx, s[b][i]);
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[b][i] *= sl2;
+          mx = fmaxf(mx, s[b][i]);
+        }
+    }
     mx = wave_max4(mx);
     const float mn = fmaxf(m, mx);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // wave-uniform
 #pragma unroll
-    for (int r = 0; r < D / 16; ++r) acc[r] *= alpha;
+      for (int r = 0; r < D / 16; ++r) acc[r] *= alpha;
+    }
     float sum = 0.f;
 #pragma unroll
-    for (int b = 0; b < NBT; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(z[b][i] - mn);
-        pw[b][i] = p;
-        sum += p;
+        s[b][i] = __builtin_amdgcn_exp2f(s[b][i] - mn);
+        sum += s[b][i];
       }
     l = l * alpha + wave_sum4(sum);
     m = mn;
+    pop.set(s);
+  };
+  auto v_stage = [&](const T* vt) __attribute__((always_inline)) {
+    const char* blk[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) blk[b] = reinterpret_cast<const char*>(vt) + 16 * b * TL::row_bytes;
+    __builtin_amdgcn_s_setprio(1);
+    pv_blocks<T, D, NB, false>(acc, blk, lo, pop);
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  auto body = [&](int G, auto bc) {
-    constexpr int B = decltype(bc)::value;
-    if (G >= nstages) return;  // workgroup-uniform
-    wait_dma();
-    issue_stage(G + 1, Buf<1 - B>{});
-    load_ops(G + 1, Buf<1 - B>{});
-    const FStage st = desc(G);
-    const T* cur = buffer(bc);
-    if (st.kind == 0) {
-      // Lightweight DC: the band's softmax, composed into Pbar
-      f32x4 sb[kKeyBlocks];
-      __builtin_amdgcn_s_setprio(2);
-      mma_dcontract_band<T, D, kKeyBlocks>(sb, cur, 16 * (w + 1), lo, qf[B]);
-      __builtin_amdgcn_s_setprio(0);
-      float mx = -INFINITY;
+  // A chunk stage s whose K is in slot P (P = 2s % 4; three half-stages in
+  // flight, so a wait leaves the two younger ones pending).
+  auto chunk = [&](auto pc, int s) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    wait_dma_except<2 * NIW>();
+    issue_half(IC<P + 3>{}, 2 * s + 3);
+    k_stage(slot(IC<P>{}), stage_row(s));
+    wait_dma_except<2 * NIW>();
+    issue_half(IC<P + 4>{}, 2 * s + 4);
+    v_stage(slot(IC<P + 1>{}));
+  };
+  // The window stages W1 (K in slot P) and W2, then the Lightweight DC
+  // band's value contraction; the last DMA (W2's V) is issued at W1's K,
+  // then the band loads (younger than it).
+  auto tail = [&](auto pc) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    const int j1 = 2 * nc;
+    wait_dma_except<2 * NIW>();
+    issue_half(IC<P + 3>{}, j1 + 3);
+    uint32_t bw[kKeyBlocks][4];
+    if constexpr (LDC) {
+      // the wave's 16 x 128 block of Pbar: word (b, 4g+i, n) of its band block
+      const int qb = (q0 >> 4) + w, nqb = (a.T + 15) >> 4;
+      const uint32_t* blk = a.band + (size_t)(qb < nqb ? qb : nqb - 1) * kBandWords;
 #pragma unroll
       for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sb[b][i] = ((mbits >> (4 * b + i)) & 1u) ? sb[b][i] * sl2 : -INFINITY;
-          mx = fmaxf(mx, sb[b][i]);
-        }
-      mx = wave_max4(mx);
-      const float mxs = mx == -INFINITY ? 0.f : mx;  // (a query past T: no key)
-      float sum = 0.f;
+        for (int i = 0; i < 4; ++i) bw[b][i] = blk[b * 256 + (4 * g + i) * 16 + n];
+    }
+    k_stage(slot(IC<P>{}), w1);
+    wait_dma_except<2 * NIW + NBAND>();
+    v_stage(slot(IC<P + 1>{}));
+    wait_dma_except<NIW + NBAND>();
+    k_stage(slot(IC<P + 2>{}), q0);
+    wait_dma_except<0>();
+    v_stage(slot(IC<P + 3>{}));
+    if constexpr (LDC) {
+      // l G Pbar V: band block b holds keys q0 + 16w - 112 + 16b .., window
+      // block w + 1 + b (W1's V below 8, else W2's)
+      const float f = l * gh;
+      f32x4 pb[kKeyBlocks];
 #pragma unroll
       for (int b = 0; b < kKeyBlocks; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sb[b][i] = __builtin_amdgcn_exp2f(sb[b][i] - mxs);
-          sum += sb[b][i];
-        }
-      sum = wave_sum4(sum);
-      const float f = sum > 0.f ? cc[B] / sum : 0.f;
+        for (int i = 0; i < 4; ++i) pb[b][i] = f * band_decode<T>(bw[b][i]);
+      BandOperand<T, kKeyBlocks> bop;
+      bop.set(pb);
+      const char* blk[kKeyBlocks];
 #pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pbar[b][i] = fmaf(f, sb[b][i], pbar[b][i]);
-    } else if (st.kind == 1 || st.kind == 3) {
-      f32x4 s[NBT];
-      __builtin_amdgcn_s_setprio(2);
-      mma_dcontract_band<T, D, NBT>(s, cur, 0, lo, qf[B]);
-      __builtin_amdgcn_s_setprio(0);
-      online(s, st.row0, st.kind == 3);
-    } else if (st.kind == 2) {
-      BandOperand<T, NBT> op;
-      op.set(pw);
-      __builtin_amdgcn_s_setprio(2);
-      tcontract_acc<T, D, NBT>(acc, cur, 0, lo, op);
-      __builtin_amdgcn_s_setprio(0);
-    } else if (st.kind == 4) {
-      if constexpr (LDC) {
-        // the Lightweight DC term joins the main weights on the wave's band
-        // blocks (tile blocks w+1 .. w+8): l G Pbar
-        const float f = l * gg[B];
-#pragma unroll
-        for (int b = 0; b < NBT; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-              const int bb = b - 1 - ww;
-              if (bb >= 0 && bb < kKeyBlocks && ww == w) x = pbar[bb][i];
-            }
-            pw[b][i] = fmaf(f, x, pw[b][i]);
-          }
+      for (int b = 0; b < kKeyBlocks; ++b) {
+        const int wb = w + 1 + b;  // wave-uniform
+        blk[b] = reinterpret_cast<const char*>(wb < 8 ? slot(IC<P + 1>{}) : slot(IC<P + 3>{})) +
+                 16 * (wb & 7) * TL::row_bytes;
       }
-      BandOperand<T, NBT> op;
-      op.set(pw);
-      __builtin_amdgcn_s_setprio(2);
-      tcontract_acc<T, D, NBT>(acc, cur, 0, lo, op);
+      __builtin_amdgcn_s_setprio(1);
+      pv_blocks<T, D, kKeyBlocks, true>(acc, blk, lo, bop);
       __builtin_amdgcn_s_setprio(0);
-      const float inv = 1.f / l;  // l >= the diagonal key's weight, > 0
-#pragma unroll
-      for (int r = 0; r < D / 16; ++r) acc[r] *= inv;
-      store_row<T, D>(pending_rows<D>(a.o, q0 + 16 * w, n, a.T, H, st.h, true, 1.f, xp), acc, g, n);
-#pragma unroll
-      for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
-      m = -1e30f;
-      l = 0.f;
     }
   };
-  for (int G = 0; G < nstages; G += 2) {
-    body(G, Buf<0>{});
-    body(G + 1, Buf<1>{});
+  int s = 0;
+  for (; s + 2 <= nc; s += 2) {  // workgroup-uniform
+    chunk(IC<0>{}, s);
+    chunk(IC<2>{}, s + 1);
   }
-  wait_dma();  // no DMA may land in LDS after the workgroup ends
+  if (nc & 1) {
+    chunk(IC<0>{}, s);
+    tail(IC<2>{});
+  } else {
+    tail(IC<0>{});
+  }
+  const float inv = 1.f / l;  // l >= the diagonal key's weight, > 0
+#pragma unroll
+  for (int r = 0; r < D / 16; ++r) acc[r] *= inv;
+  store_row<T, D>(pending_rows<D>(a.o, tw, n, a.T, H, h, true, 1.f, s_xp + w * 512), acc, g, n);
 }
 
 template <typename T, int D>
-static hipError_t launch_fused(const FusedArgs& a, bool ldc, hipStream_t st) {
-  const int nblk = (a.T + kFBQ - 1) / kFBQ;
+static hipError_t launch_attn(const AttnArgs& a, bool ldc, hipStream_t st) {
+  const int ntile = (a.T + kABQ - 1) / kABQ;
+  const dim3 grid(ntile * a.H), block(kANW * kWave);
   if (ldc)
-    hipLaunchKernelGGL((fused_fwd_kernel<T, D, true>), dim3(nblk), dim3(kFNW * kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((fused_fwd_kernel<T, D, false>), dim3(nblk), dim3(kFNW * kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t fused_fwd_dispatch(int d, const FusedArgs& a, bool ldc, hipStream_t st) {
-  if (d == 128) return launch_fused<bf16_t, 128>(a, ldc, st);
-  return launch_fused<bf16_t, 64>(a, ldc, st);
+size_t run_blocks(int64_t T) { return (size_t)((T + kRunBlock - 1) / kRunBlock); }
+
+hipError_t run_starts_dispatch(const int32_t* doc, int T, int* last, int* rs, hipStream_t st) {
+  const int nb = (int)run_blocks(T);
+  hipLaunchKernelGGL(run_marks_kernel, dim3(nb), dim3(256), 0, st, doc, T, last);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(run_starts_kernel, dim3(nb), dim3(256), 0, st, doc, T, last, rs);
+  return hipGetLastError();
+}
+
+hipError_t attn_fwd_dispatch(int d, const AttnArgs& a, bool ldc, hipStream_t st) {
+  if (d == 128) return launch_attn<bf16_t, 128>(a, ldc, st);
+  return launch_attn<bf16_t, 64>(a, ldc, st);
 }
 
 }  // namespace ldc

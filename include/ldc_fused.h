@@ -24,6 +24,15 @@
  * validated before any HIP call; errors return a non-zero ldc_status with no
  * side effects.  The main attention's work grows with the document length
  * (every query reads its whole run).
+ *
+ * Workspace (device memory, 16-byte aligned, at least the size the matching
+ * *_workspace_bytes call returns, contents need not be initialised, used
+ * only by work enqueued by the call): the first ldc_saved_bytes(dtype, T, H,
+ * d, window) bytes of the fused call's workspace receive the Lightweight DC
+ * layer's saved state exactly as ldc_fwd writes it (the composed-map band
+ * and the softmax statistics), so it can be passed to ldc_bwd as `saved`
+ * until the next call that writes it; the rest holds every token's run start.
+ * Too small or missing: LDC_ERR_WORKSPACE.
  */
 #ifndef LDC_FUSED_H_
 #define LDC_FUSED_H_
@@ -37,17 +46,24 @@
 extern "C" {
 #endif
 
+/* Workspace bytes of ldc_fused_fwd (0 for invalid arguments or T == 0). */
+size_t ldc_fused_fwd_workspace_bytes(int dtype, int64_t T, int H, int d, int window);
+
 /* The block's attention output O = M + the Lightweight DC layer (above). */
 int ldc_fused_fwd(int dtype, int64_t T, int H, int d, int window, float scale,
                   const void* q, const void* k, const void* v,
                   const float* c, const float* g, const int32_t* doc_ids,
-                  float* o, void* stream);
+                  float* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of ldc_main_attention_fwd (0 for T <= 0 or T > 2^30). */
+size_t ldc_main_attention_workspace_bytes(int64_t T);
 
 /* The main attention M alone (the same kernel without the Lightweight DC
  * terms), for comparison and as the unfused block's first half. */
 int ldc_main_attention_fwd(int dtype, int64_t T, int H, int d, float scale,
                            const void* q, const void* k, const void* v,
-                           const int32_t* doc_ids, float* o, void* stream);
+                           const int32_t* doc_ids, float* o,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

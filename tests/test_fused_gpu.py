@@ -12,6 +12,8 @@ from tests.helpers import assert_close, to_np
 pytestmark = pytest.mark.gpu
 
 REPEATED = np.array([0] * 100 + [1] * 50 + [0] * 200 + [2] * 106, dtype=np.int32)  # id 0 twice
+# run boundaries on and beside the run-start pass's 1024-token block edges
+EDGES = np.repeat(np.arange(7, dtype=np.int32), [1023, 1, 1025, 2047, 1, 3000, 130])
 
 SMALL = [  # (T, H, d, window, docs, seed, c_kind)
     (1, 1, 64, 112, ("single",), 0, "normal0.5"),
@@ -24,6 +26,7 @@ SMALL = [  # (T, H, d, window, docs, seed, c_kind)
     (2049, 6, 128, 112, ("geometric", 1024), 7, "normal0.5"),
     (456, 6, 64, 112, ("fixed", REPEATED), 8, "normal0.5"),      # a repeated id is a new document
     (129, 7, 128, 112, ("geometric", 40), 9, "normal0.5"),     # H = 7
+    (len(EDGES), 2, 64, 112, ("fixed", EDGES), 10, "normal0.5"),
 ]
 
 
@@ -123,3 +126,33 @@ def test_empty(fz):
     doc = torch.zeros(0, dtype=torch.int32, device="cuda")
     assert fz.fwd(q, q, q, c, c, doc).shape == (0, 6, 128)
     assert fz.main_fwd(q, q, q, doc).shape == (0, 6, 128)
+
+
+def test_saved_state_matches_layer_forward(fz, ldc):
+    """The fused call's workspace holds the Lightweight DC layer's saved state
+    exactly as ldc_fwd writes it (the same score pass), so the backward can
+    take it."""
+    import torch
+    w = wl.make_workload(777, 6, 128, docs=("geometric", 200), seed=33, with_do=False)
+    q, k, v, c, g, doc = inputs(w)
+    _, saved = fz.fwd(q, k, v, c, g, doc, window=w.window, scale=w.scale, save=True)
+    _, ref = ldc.fwd(q, k, v, c, g, doc, window=w.window, scale=w.scale, save=True)
+    torch.cuda.synchronize()
+    n = ldc.saved_bytes(ldc.LDC_BF16, w.T, w.H, w.d, w.window)
+    assert torch.equal(saved[:n], ref.view(torch.uint8).reshape(-1)[:n])
+
+
+def test_run_start_lookback(fz):
+    """A run longer than 256 run-start blocks (262,144 tokens): the look-back
+    over the block summaries takes a second round."""
+    import torch
+    T = 270000
+    docs = np.zeros(T, dtype=np.int32)
+    docs[5:] = 1
+    w = wl.make_workload(T, 1, 64, docs=("fixed", docs), seed=34, with_do=False)
+    q, k, v, c, g, doc = inputs(w)
+    m = fz.main_fwd(q, k, v, doc, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = [0, 4, 5, 6, 1023, 262143, 262144, 262150, T - 1]
+    ref = fo.main_attention(w.q, w.k, w.v, w.doc, w.scale, queries=rows)
+    assert_close("main rows", to_np(m)[rows], ref, "bf16")
