@@ -210,10 +210,52 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
     constexpr int I = decltype(c)::value & 3;
     return I == 0 ? s_r0 : I == 1 ? s_r1 : I == 2 ? s_r2 : s_r3;
   };
-  // DMA of half-stage j (j % 4 == I) into its slot
+  // DMA of half-stage j (j % 4 == I) into its slot.  The lane offsets of an
+  // in-range tile are fixed for the item; only the buffer resource and, for
+  // a tile with rows outside [0, T) (those read as zero), the offsets change.
+  // The DMA instructions are the same straight-line sequence either way.
+  constexpr int RPI = TL::rows_per_inst, NI = R / RPI;
+  const uint32_t rstride = (uint32_t)H * D * sizeof(T);
+  uint32_t voff[NIW];
+#pragma unroll
+  for (int u = 0; u < NIW; ++u) {
+    const int jj = (w + u * NW < NI) ? w + u * NW : NI - 1;
+    const int rl = jj * RPI + lane / TL::chunks;
+    voff[u] = (uint32_t)rl * rstride + (uint32_t)TL::pos(rl, lane % TL::chunks) * 16u;
+  }
   auto issue_half = [&](auto c, int j) __attribute__((always_inline)) {
-    issue_tile<T, D, R, NW>(slot(c), (decltype(c)::value & 1) ? v : k, stage_row(j >> 1), a.T, H, h);
+    const T* src = (decltype(c)::value & 1) ? v : k;
+    const int row0 = stage_row(j >> 1);
+    i32x4 rsrc;
+    uint32_t vo[NIW];
+    if (row0 >= 0 && row0 + R <= a.T) {  // workgroup-uniform
+      rsrc = make_rsrc(src + ((size_t)row0 * H + h) * D, (uint32_t)(R - 1) * rstride + D * sizeof(T));
+#pragma unroll
+      for (int u = 0; u < NIW; ++u) vo[u] = voff[u];
+    } else {
+      const int lo_r = row0 > 0 ? row0 : 0;
+      const int hi_r = row0 + R < a.T ? row0 + R : a.T;
+      const uint32_t bytes = hi_r > lo_r ? (uint32_t)(hi_r - 1 - lo_r) * rstride + D * sizeof(T) : 0u;
+      rsrc = make_rsrc(src + ((size_t)(hi_r > lo_r ? lo_r : 0) * H + h) * D, bytes);
+#pragma unroll
+      for (int u = 0; u < NIW; ++u) {
+        const int jj = (w + u * NW < NI) ? w + u * NW : NI - 1;
+        const int sr = row0 + jj * RPI + lane / TL::chunks;
+        // out of range: an offset at the end of the (possibly empty) buffer reads zero
+        vo[u] = (sr >= lo_r && sr < hi_r) ? voff[u] - (uint32_t)(lo_r - row0) * rstride : bytes;
+      }
+    }
+    char* base = reinterpret_cast<char*>(slot(c));
+#pragma unroll
+    for (int u = 0; u < NIW; ++u) {
+      const int jj = (w + u * NW < NI) ? w + u * NW : NI - 1;
+      ldc_buffer_load_lds(rsrc, (lds_u32_ptr)(base + jj * 1024), 16, (int)vo[u], 0, 0, 0);
+    }
   };
+  // a stage needs masking when it holds keys below the wave's latest run
+  // start (run starts never decrease, so that of its last query) or past
+  // the wave's first query
+  const int kmax = __builtin_amdgcn_readfirstlane(a.rs[tw + 15 < a.T ? tw + 15 : a.T - 1]);
   issue_half(IC<0>{}, 0);
   issue_half(IC<1>{}, 1);
   issue_half(IC<2>{}, 2);
@@ -221,10 +263,6 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
   // said here, the compiler need not drain the DMA before the stage loop
   __builtin_amdgcn_s_waitcnt(((3 * NIW) & 15) | (((3 * NIW) >> 4) << 14) | (7 << 4) | (15 << 8));
 
-  // a stage needs masking when it holds keys below the wave's latest run
-  // start (run starts never decrease, so that of its last query) or past
-  // the wave's first query
-  const int kmax = __builtin_amdgcn_readfirstlane(a.rs[tw + 15 < a.T ? tw + 15 : a.T - 1]);
 
   f32x4 acc[D / 16];
 #pragma unroll
@@ -238,27 +276,22 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
     __builtin_amdgcn_s_setprio(1);
     mma_dcontract_band<T, D, NB>(s, kt, 0, lo, qf);
     __builtin_amdgcn_s_setprio(0);
-    float mx = -INFINITY;
     if (row0 < kmax || row0 + R - 1 > tw) {  // wave-uniform
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = row0 + 16 * b + 4 * g + i;
-          s[b][i] = (key >= kslo && key <= t) ? s[b][i] * sl2 : -INFINITY;
-          mx = fmaxf(mx, s[b][i]);
-        }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s[b][i] *= sl2;
-          mx = fmaxf(mx, s[b][i]);
+          s[b][i] = (key >= kslo && key <= t) ? s[b][i] : -INFINITY;
         }
     }
+    // the scale is positive: the max of the raw scores gives the max of the
+    // scaled ones, and the scaling joins the exponent's FMA
+    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mx = fmaxf(mx, fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])));
     mx = wave_max4(mx);
-    const float mn = fmaxf(m, mx);
+    const float mn = fmaxf(m, mx * sl2);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // wave-uniform
 #pragma unroll
@@ -269,7 +302,7 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[b][i] = __builtin_amdgcn_exp2f(s[b][i] - mn);
+        s[b][i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], sl2, -mn));
         sum += s[b][i];
       }
     l = l * alpha + wave_sum4(sum);
