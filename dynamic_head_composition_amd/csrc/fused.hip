@@ -161,6 +161,63 @@ __device__ __forceinline__ void pv_blocks(f32x4 (&acc)[D / 16], const char* cons
   }
 }
 
+// s[b] = (16 keys of block b of a staged tile) x (this lane's query row),
+// contracted over the head dimension: the transposed score block, lane (g, n)
+// holding keys 4g..4g+3 of query n.  Each block's K fragments are read just
+// before its MFMAs (no scheduling pins), so the caller's independent VALU
+// work can fill the MFMA shadow.
+template <typename T, int D, int NB>
+__device__ __forceinline__ void score_band(f32x4 (&s)[NB], const T* tile, const LaneOffsets<T, D>& lo,
+                                           const RowFrag<T, D>& f) {
+  using TL = Tile<T, D>;
+  constexpr int KK = D / 32;
+  const char* base = reinterpret_cast<const char*>(tile);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    bf16x8 u[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      u[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(base + 16 * b * TL::row_bytes + lo.dk[kk]));
+    f32x4 c = zero4();
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) c = mma(u[kk], f.v[kk], c);
+    s[b] = c;
+  }
+}
+
+// acc += V^T P over the NB 16-key blocks of one staged V tile (P the hi part
+// of a band operand in accumulator layout), one column group of the output at
+// a time: its transposed V reads, then its MFMAs (no scheduling pins).
+template <typename T, int D, int NB>
+__device__ __forceinline__ void pv_stream(f32x4 (&acc)[D / 16], const T* vt, const LaneOffsets<T, D>& lo,
+                                          const BandOperand<T, NB>& P) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_v4;
+  using TL = Tile<T, D>;
+  const char* base = reinterpret_cast<const char*>(vt);
+#pragma unroll
+  for (int p = 0; p < D / 32; ++p) {
+    bf16x8 a[NB / 2][2];
+#pragma unroll
+    for (int ks = 0; ks < NB / 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int off = lo.tr[p] ^ (8 * e);
+        const bf16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + 32 * ks * TL::row_bytes + off));
+        const bf16x4 h4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + (32 * ks + 16) * TL::row_bytes + off));
+        a[ks][e] = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    f32x4 c0 = acc[2 * p], c1 = acc[2 * p + 1];
+#pragma unroll
+    for (int ks = 0; ks < NB / 2; ++ks) {
+      c0 = mma(a[ks][0], P.hi[ks], c0);
+      c1 = mma(a[ks][1], P.hi[ks], c1);
+    }
+    acc[2 * p] = c0;
+    acc[2 * p + 1] = c1;
+  }
+}
+
 template <typename T, int D, bool LDC>
 __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NW = kANW, BQ = kABQ, R = kARows, NB = kABlocks;
@@ -269,13 +326,13 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
   for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
   float m = -1e30f, l = 0.f;  // running max (log2 units; finite start) and sum
   BandOperand<T, NB> pop;     // the current stage's P (its hi part is used)
+  const int NS = nc + 2;      // stages; the last two are the window stages
 
-  // scores of a K stage and the online-softmax update; leaves P in pop
-  auto k_stage = [&](const T* kt, int row0) __attribute__((always_inline)) {
-    f32x4 s[NB];
-    __builtin_amdgcn_s_setprio(1);
-    mma_dcontract_band<T, D, NB>(s, kt, 0, lo, qf);
-    __builtin_amdgcn_s_setprio(0);
+  // Masking of stage s's scores: keys below the query's run start or past
+  // the query.  Needed only where the stage holds keys below the wave's
+  // latest run start (run starts never decrease: that of its last query) or
+  // past the wave's first query.
+  auto mask = [&](f32x4 (&s)[NB], int row0) __attribute__((always_inline)) {
     if (row0 < kmax || row0 + R - 1 > tw) {  // wave-uniform
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -285,18 +342,19 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
           s[b][i] = (key >= kslo && key <= t) ? s[b][i] : -INFINITY;
         }
     }
-    // the scale is positive: the max of the raw scores gives the max of the
-    // scaled ones, and the scaling joins the exponent's FMA
+  };
+  // Online softmax of masked scores; leaves P in pop.  The scale is
+  // positive: the max of the raw scores gives the max of the scaled ones, and
+  // the scaling joins the exponent's FMA.
+  auto softmax = [&](f32x4 (&s)[NB]) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < NB; ++b) mx = fmaxf(mx, fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])));
     mx = wave_max4(mx);
     const float mn = fmaxf(m, mx * sl2);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // wave-uniform
 #pragma unroll
-      for (int r = 0; r < D / 16; ++r) acc[r] *= alpha;
-    }
+    for (int r = 0; r < D / 16; ++r) acc[r] *= alpha;
     float sum = 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -309,37 +367,28 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
     m = mn;
     pop.set(s);
   };
-  auto v_stage = [&](const T* vt) __attribute__((always_inline)) {
-    const char* blk[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) blk[b] = reinterpret_cast<const char*>(vt) + 16 * b * TL::row_bytes;
-    __builtin_amdgcn_s_setprio(1);
-    pv_blocks<T, D, NB, false>(acc, blk, lo, pop);
-    __builtin_amdgcn_s_setprio(0);
-  };
+  auto v_stage = [&](const T* vt) __attribute__((always_inline)) { pv_stream<T, D, NB>(acc, vt, lo, pop); };
 
-  // A chunk stage s whose K is in slot P (P = 2s % 4; three half-stages in
-  // flight, so a wait leaves the two younger ones pending).
-  auto chunk = [&](auto pc, int s) __attribute__((always_inline)) {
+  // Software pipeline, one barrier per stage: stage s's softmax and value
+  // contraction run beside the score MFMAs of stage s+1, whose K is already
+  // staged.  On entering iteration s the ring holds V(s) and K(s+1) (issued
+  // one iteration earlier); the iteration then issues V(s+1) and K(s+2) into
+  // the slots of V(s-1) and K(s), both consumed before the barrier.
+  f32x4 sa[NB], sb[NB];
+  wait_dma_except<2 * NIW>();  // K(0)
+  score_band<T, D, NB>(sa, slot(IC<0>{}), lo, qf);
+  uint32_t bw[kKeyBlocks][4];  // the wave's Pbar band words (Lightweight DC)
+  // iteration s with K(s) in slot P; LAST: the final stage (no next scores;
+  // the band words load here, beside its softmax and value contraction)
+  auto iter = [&](auto pc, auto lastc, int s, f32x4 (&cur)[NB], f32x4 (&nxt)[NB]) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
-    wait_dma_except<2 * NIW>();
-    issue_half(IC<P + 3>{}, 2 * s + 3);
-    k_stage(slot(IC<P>{}), stage_row(s));
-    wait_dma_except<2 * NIW>();
-    issue_half(IC<P + 4>{}, 2 * s + 4);
-    v_stage(slot(IC<P + 1>{}));
-  };
-  // The window stages W1 (K in slot P) and W2, then the Lightweight DC
-  // band's value contraction; the last DMA (W2's V) is issued at W1's K,
-  // then the band loads (younger than it).
-  auto tail = [&](auto pc) __attribute__((always_inline)) {
-    constexpr int P = decltype(pc)::value;
-    const int j1 = 2 * nc;
-    wait_dma_except<2 * NIW>();
-    issue_half(IC<P + 3>{}, j1 + 3);
-    uint32_t bw[kKeyBlocks][4];
-    if constexpr (LDC) {
-      // the wave's 16 x 128 block of Pbar: word (b, 4g+i, n) of its band block
+    constexpr bool LAST = decltype(lastc)::value;
+    wait_dma_except<0>();
+    if constexpr (!LAST) {
+      issue_half(IC<P + 3>{}, 2 * s + 3);  // V(s+1)
+      if (s + 2 < NS) issue_half(IC<P + 4>{}, 2 * s + 4);  // K(s+2); workgroup-uniform
+    } else if constexpr (LDC) {
+      // word (b, 4g+i, n) of the wave's 16 x 128 band block
       const int qb = (q0 >> 4) + w, nqb = (a.T + 15) >> 4;
       const uint32_t* blk = a.band + (size_t)(qb < nqb ? qb : nqb - 1) * kBandWords;
 #pragma unroll
@@ -347,16 +396,32 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) bw[b][i] = blk[b * 256 + (4 * g + i) * 16 + n];
     }
-    k_stage(slot(IC<P>{}), w1);
-    wait_dma_except<2 * NIW + NBAND>();
+    mask(cur, stage_row(s));
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (!LAST) score_band<T, D, NB>(nxt, slot(IC<P + 2>{}), lo, qf);
+    softmax(cur);
     v_stage(slot(IC<P + 1>{}));
-    wait_dma_except<NIW + NBAND>();
-    k_stage(slot(IC<P + 2>{}), q0);
-    wait_dma_except<0>();
-    v_stage(slot(IC<P + 3>{}));
-    if constexpr (LDC) {
-      // l G Pbar V: band block b holds keys q0 + 16w - 112 + 16b .., window
-      // block w + 1 + b (W1's V below 8, else W2's)
+    __builtin_amdgcn_s_setprio(0);
+  };
+  const std::false_type mid;
+  const std::true_type last;
+  int s = 0;
+  for (; s + 2 < NS; s += 2) {  // workgroup-uniform
+    iter(IC<0>{}, mid, s, sa, sb);
+    iter(IC<2>{}, mid, s + 1, sb, sa);
+  }
+  if (NS - s == 2) {
+    iter(IC<0>{}, mid, s, sa, sb);
+    iter(IC<2>{}, last, s + 1, sb, sa);
+  } else {
+    iter(IC<0>{}, last, s, sa, sb);
+  }
+  if constexpr (LDC) {
+    // l G Pbar V over the band: block b holds keys q0 + 16w - 112 + 16b ..,
+    // window block w + 1 + b (W1's V below 8, else W2's); W1's K sat in slot
+    // PW = 2 (NS - 2) % 4, its V in PW + 1 and W2's V in PW + 3
+    auto band_tail = [&](auto pc) __attribute__((always_inline)) {
+      constexpr int PW = decltype(pc)::value;
       const float f = l * gh;
       f32x4 pb[kKeyBlocks];
 #pragma unroll
@@ -369,24 +434,17 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
 #pragma unroll
       for (int b = 0; b < kKeyBlocks; ++b) {
         const int wb = w + 1 + b;  // wave-uniform
-        blk[b] = reinterpret_cast<const char*>(wb < 8 ? slot(IC<P + 1>{}) : slot(IC<P + 3>{})) +
+        blk[b] = reinterpret_cast<const char*>(wb < 8 ? slot(IC<PW + 1>{}) : slot(IC<PW + 3>{})) +
                  16 * (wb & 7) * TL::row_bytes;
       }
       __builtin_amdgcn_s_setprio(1);
       pv_blocks<T, D, kKeyBlocks, true>(acc, blk, lo, bop);
       __builtin_amdgcn_s_setprio(0);
-    }
-  };
-  int s = 0;
-  for (; s + 2 <= nc; s += 2) {  // workgroup-uniform
-    chunk(IC<0>{}, s);
-    chunk(IC<2>{}, s + 1);
-  }
-  if (nc & 1) {
-    chunk(IC<0>{}, s);
-    tail(IC<2>{});
-  } else {
-    tail(IC<0>{});
+    };
+    if (NS & 1)
+      band_tail(IC<2>{});
+    else
+      band_tail(IC<0>{});
   }
   const float inv = 1.f / l;  // l >= the diagonal key's weight, > 0
 #pragma unroll
