@@ -163,6 +163,56 @@ def blas_threads() -> int:
         return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
 
 
+class TimingEvent:
+    """A HIP event for timing only, recorded on torch's current stream (the
+    stream the library's kernels are enqueued on).  Created with
+    hipEventDisableSystemFence: recording it writes a timestamp without the
+    system-scope fence (L2 write-back and invalidate) of a default event,
+    which measured ~3 us per record at the GPT-2 small step and slowed the
+    kernels after it.  elapsed_time(other) in ms, like torch's events."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            lib = ctypes.CDLL("libamdhip64.so")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ev = ctypes.c_void_p()
+        st = self._lib().hipEventCreateWithFlags(ctypes.byref(self._ev), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self):
+        import ctypes
+        import torch
+        st = self._lib().hipEventRecord(self._ev, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        st = self._lib().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and getattr(self, "_ev", None):
+            self._hip.hipEventDestroy(self._ev)
+
+
 def stats_us(samples_ms) -> dict:
     """Median and interquartile range (µs) of per-step event times."""
     a = np.asarray(samples_ms, dtype=np.float64) * 1e3
@@ -338,7 +388,7 @@ def bench_dcmha(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
@@ -498,7 +548,7 @@ def bench_fused(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         evs[i][0].record()
@@ -511,7 +561,7 @@ def bench_fused(args):
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     fst = stats_us([e[0].elapsed_time(e[1]) for e in evs])
     # the unfused pair, for comparison (not part of the step)
-    uevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    uevs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         unfused(uevs[i])
     torch.cuda.synchronize()
@@ -614,7 +664,7 @@ def bench_cg(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
@@ -704,7 +754,7 @@ def bench_mudd(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
@@ -830,7 +880,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
