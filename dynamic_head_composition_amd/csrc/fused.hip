@@ -109,63 +109,23 @@ __global__ __launch_bounds__(256) void run_starts_kernel(const int32_t* __restri
 // ---------------------------------------------------------------------------
 constexpr int kANW = 8;                // waves per workgroup
 constexpr int kABQ = 16 * kANW;        // 128 queries per tile
-constexpr int kARows = 128;            // keys per stage
-constexpr int kABlocks = kARows / 16;  // 8 key blocks per stage
+constexpr int kARows = 64;             // keys per stage
+constexpr int kABlocks = kARows / 16;  // 4 key blocks per stage
 
 template <int I>
 using IC = std::integral_constant<int, I>;
 
-// acc += X^T P over NB 16-row blocks of staged tiles, block b starting at LDS
-// byte address blk[b] (X a tile's rows, P a band operand in accumulator
-// layout; HILO: P carried as hi + lo bf16 parts, else hi only).  The LDS
-// transpose reads of column group p+1 are issued ahead of the MFMAs of group
-// p; each group's two chains alternate.
-template <typename T, int D, int NB, bool HILO>
-__device__ __forceinline__ void pv_blocks(f32x4 (&acc)[D / 16], const char* const (&blk)[NB],
-                                          const LaneOffsets<T, D>& lo, const BandOperand<T, NB>& P) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_v4;
-  constexpr int NP = D / 32;
-  constexpr int PER = HILO ? 4 : 2;  // MFMAs per (p, ks)
-  bf16x8 a[NP][NB / 2][2];
-#pragma unroll
-  for (int p = 0; p < NP; ++p)
-#pragma unroll
-    for (int ks = 0; ks < NB / 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int off = lo.tr[p] ^ (8 * e);
-        const bf16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(blk[2 * ks] + off));
-        const bf16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(blk[2 * ks + 1] + off));
-        a[p][ks][e] = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    f32x4 c0 = acc[2 * p], c1 = acc[2 * p + 1];
-#pragma unroll
-    for (int ks = 0; ks < NB / 2; ++ks) {
-      c0 = mma(a[p][ks][0], P.hi[ks], c0);
-      c1 = mma(a[p][ks][1], P.hi[ks], c1);
-      if constexpr (HILO) {
-        c0 = mma(a[p][ks][0], P.lo[ks], c0);
-        c1 = mma(a[p][ks][1], P.lo[ks], c1);
-      }
-    }
-    acc[2 * p] = c0;
-    acc[2 * p + 1] = c1;
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * NB, 0);
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    if (p + 1 < NP) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NB, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, PER * NB / 2, 0);
-  }
+// The 32-bit LDS address of a pointer into a __shared__ array.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_offset(const T* p) {
+  typedef const __attribute__((address_space(3))) char* lds_cptr;
+  return (uint32_t)(uintptr_t)(lds_cptr)(const void*)p;
 }
 
 // s[b] = (16 keys of block b of a staged tile) x (this lane's query row),
 // contracted over the head dimension: the transposed score block, lane (g, n)
 // holding keys 4g..4g+3 of query n.  Each block's K fragments are read just
-// before its MFMAs (no scheduling pins), so the caller's independent VALU
-// work can fill the MFMA shadow.
+// before its MFMAs.
 template <typename T, int D, int NB>
 __device__ __forceinline__ void score_band(f32x4 (&s)[NB], const T* tile, const LaneOffsets<T, D>& lo,
                                            const RowFrag<T, D>& f) {
@@ -185,15 +145,14 @@ __device__ __forceinline__ void score_band(f32x4 (&s)[NB], const T* tile, const 
   }
 }
 
-// acc += V^T P over the NB 16-key blocks of one staged V tile (P the hi part
-// of a band operand in accumulator layout), one column group of the output at
-// a time: its transposed V reads, then its MFMAs (no scheduling pins).
-template <typename T, int D, int NB>
-__device__ __forceinline__ void pv_stream(f32x4 (&acc)[D / 16], const T* vt, const LaneOffsets<T, D>& lo,
-                                          const BandOperand<T, NB>& P) {
+// acc += X^T P over NB 16-row blocks of staged tiles, block b starting at
+// LDS byte address blk[b] (X the rows, P a band operand in accumulator
+// layout; HILO: P carried as hi + lo bf16 parts, else hi only), one column
+// group of the output at a time: its transposed reads, then its MFMAs.
+template <typename T, int D, int NB, bool HILO>
+__device__ __forceinline__ void pv_stream(f32x4 (&acc)[D / 16], const char* const (&blk)[NB],
+                                          const LaneOffsets<T, D>& lo, const BandOperand<T, NB>& P) {
   typedef __attribute__((address_space(3))) bf16x4 lds_v4;
-  using TL = Tile<T, D>;
-  const char* base = reinterpret_cast<const char*>(vt);
 #pragma unroll
   for (int p = 0; p < D / 32; ++p) {
     bf16x8 a[NB / 2][2];
@@ -202,9 +161,8 @@ __device__ __forceinline__ void pv_stream(f32x4 (&acc)[D / 16], const T* vt, con
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int off = lo.tr[p] ^ (8 * e);
-        const bf16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + 32 * ks * TL::row_bytes + off));
-        const bf16x4 h4 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + (32 * ks + 16) * TL::row_bytes + off));
+        const bf16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(blk[2 * ks] + off));
+        const bf16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(blk[2 * ks + 1] + off));
         a[ks][e] = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     f32x4 c0 = acc[2 * p], c1 = acc[2 * p + 1];
@@ -212,17 +170,23 @@ __device__ __forceinline__ void pv_stream(f32x4 (&acc)[D / 16], const T* vt, con
     for (int ks = 0; ks < NB / 2; ++ks) {
       c0 = mma(a[ks][0], P.hi[ks], c0);
       c1 = mma(a[ks][1], P.hi[ks], c1);
+      if constexpr (HILO) {
+        c0 = mma(a[ks][0], P.lo[ks], c0);
+        c1 = mma(a[ks][1], P.lo[ks], c1);
+      }
     }
     acc[2 * p] = c0;
     acc[2 * p + 1] = c1;
   }
 }
 
+// One workgroup per (128-query tile, head).  Two workgroups share a CU: the
+// ring (four 64-key slots) is 64 KB at d = 128 and the kernel keeps to 128
+// VGPRs, so each SIMD holds four waves.
 template <typename T, int D, bool LDC>
-__global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kANW * kWave, 4) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NW = kANW, BQ = kABQ, R = kARows, NB = kABlocks;
   constexpr int NIW = tile_insts_per_wave<T, D, R, NW>();  // DMA instructions per wave per half-stage
-  constexpr int NBAND = LDC ? kKeyBlocks * 4 : 0;          // band loads per lane
   using TL = Tile<T, D>;
   // the ring: slot i holds half-stage j with j % 4 == i (K of stage s is
   // half-stage 2s, V of stage s is 2s + 1).  Four separate arrays, always
@@ -232,7 +196,10 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
   __shared__ __attribute__((aligned(1024))) T s_r1[R * D];
   __shared__ __attribute__((aligned(1024))) T s_r2[R * D];
   __shared__ __attribute__((aligned(1024))) T s_r3[R * D];
-  __shared__ __attribute__((aligned(16))) float s_xp[NW * 512];
+  // row-store scratch (2 KB per wave): slot 0 once the ring is done where a
+  // slot holds it (d = 128), else an array of its own
+  constexpr bool kXpInRing = R * D * (int)sizeof(T) >= NW * 512 * (int)sizeof(float);
+  __shared__ __attribute__((aligned(16))) float s_xp[kXpInRing ? 4 : NW * 512];
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
@@ -257,20 +224,22 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
   float gh = 0.f;
   if constexpr (LDC) gh = a.g[(size_t)tc * H + h];
 
-  // stages: chunks of R keys from (at or before) ks0 up to q0-129, then
-  // W1 = [q0-128, q0) and W2 = [q0, q0+128)
-  const int w1 = q0 - R;
+  // stages: chunks of R keys from (at or before) ks0 up to q0-129, then the
+  // four window stages [q0-128, q0+128)
+  const int w1 = q0 - 2 * R;
   const int span = w1 - ks0;
   const int nc = span > 0 ? (span + R - 1) / R : 0;
+  const int NS = nc + 4;
   auto stage_row = [&](int s) __attribute__((always_inline)) { return w1 - R * (nc - s); };
   auto slot = [&](auto c) __attribute__((always_inline)) -> T* {
     constexpr int I = decltype(c)::value & 3;
     return I == 0 ? s_r0 : I == 1 ? s_r1 : I == 2 ? s_r2 : s_r3;
   };
-  // DMA of half-stage j (j % 4 == I) into its slot.  The lane offsets of an
+  // DMA of R rows of `src` from row0 into a slot.  The lane offsets of an
   // in-range tile are fixed for the item; only the buffer resource and, for
-  // a tile with rows outside [0, T) (those read as zero), the offsets change.
-  // The DMA instructions are the same straight-line sequence either way.
+  // a tile with rows outside [lim0, lim1) (those read as zero), the offsets
+  // change.  The DMA instructions are the same straight-line sequence either
+  // way, so the number in flight is always NIW per call.
   constexpr int RPI = TL::rows_per_inst, NI = R / RPI;
   const uint32_t rstride = (uint32_t)H * D * sizeof(T);
   uint32_t voff[NIW];
@@ -280,18 +249,16 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
     const int rl = jj * RPI + lane / TL::chunks;
     voff[u] = (uint32_t)rl * rstride + (uint32_t)TL::pos(rl, lane % TL::chunks) * 16u;
   }
-  auto issue_half = [&](auto c, int j) __attribute__((always_inline)) {
-    const T* src = (decltype(c)::value & 1) ? v : k;
-    const int row0 = stage_row(j >> 1);
+  auto issue_rows = [&](auto c, const T* src, int row0, int lim1) __attribute__((always_inline)) {
     i32x4 rsrc;
     uint32_t vo[NIW];
-    if (row0 >= 0 && row0 + R <= a.T) {  // workgroup-uniform
+    if (row0 >= 0 && row0 + R <= lim1) {  // workgroup-uniform
       rsrc = make_rsrc(src + ((size_t)row0 * H + h) * D, (uint32_t)(R - 1) * rstride + D * sizeof(T));
 #pragma unroll
       for (int u = 0; u < NIW; ++u) vo[u] = voff[u];
     } else {
       const int lo_r = row0 > 0 ? row0 : 0;
-      const int hi_r = row0 + R < a.T ? row0 + R : a.T;
+      const int hi_r = row0 + R < lim1 ? row0 + R : lim1;
       const uint32_t bytes = hi_r > lo_r ? (uint32_t)(hi_r - 1 - lo_r) * rstride + D * sizeof(T) : 0u;
       rsrc = make_rsrc(src + ((size_t)(hi_r > lo_r ? lo_r : 0) * H + h) * D, bytes);
 #pragma unroll
@@ -309,6 +276,12 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
       ldc_buffer_load_lds(rsrc, (lds_u32_ptr)(base + jj * 1024), 16, (int)vo[u], 0, 0, 0);
     }
   };
+  // half-stage j of the loop; past the last stage it reads nothing (zeros)
+  const int lim_loop = q0 + BQ < a.T ? q0 + BQ : a.T;
+  auto issue_half = [&](auto c, int j) __attribute__((always_inline)) {
+    const T* src = (decltype(c)::value & 1) ? v : k;
+    issue_rows(c, src, stage_row(j >> 1), j < 2 * NS ? lim_loop : -(1 << 30));
+  };
   // a stage needs masking when it holds keys below the wave's latest run
   // start (run starts never decrease, so that of its last query) or past
   // the wave's first query
@@ -320,19 +293,18 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
   // said here, the compiler need not drain the DMA before the stage loop
   __builtin_amdgcn_s_waitcnt(((3 * NIW) & 15) | (((3 * NIW) >> 4) << 14) | (7 << 4) | (15 << 8));
 
-
   f32x4 acc[D / 16];
 #pragma unroll
   for (int r = 0; r < D / 16; ++r) acc[r] = zero4();
   float m = -1e30f, l = 0.f;  // running max (log2 units; finite start) and sum
   BandOperand<T, NB> pop;     // the current stage's P (its hi part is used)
-  const int NS = nc + 2;      // stages; the last two are the window stages
 
-  // Masking of stage s's scores: keys below the query's run start or past
-  // the query.  Needed only where the stage holds keys below the wave's
-  // latest run start (run starts never decrease: that of its last query) or
-  // past the wave's first query.
-  auto mask = [&](f32x4 (&s)[NB], int row0) __attribute__((always_inline)) {
+  // scores of a K stage and the online-softmax update; leaves P in pop
+  auto k_stage = [&](const T* kt, int row0) __attribute__((always_inline)) {
+    f32x4 s[NB];
+    __builtin_amdgcn_s_setprio(1);
+    score_band<T, D, NB>(s, kt, lo, qf);
+    __builtin_amdgcn_s_setprio(0);
     if (row0 < kmax || row0 + R - 1 > tw) {  // wave-uniform
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -342,19 +314,18 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
           s[b][i] = (key >= kslo && key <= t) ? s[b][i] : -INFINITY;
         }
     }
-  };
-  // Online softmax of masked scores; leaves P in pop.  The scale is
-  // positive: the max of the raw scores gives the max of the scaled ones, and
-  // the scaling joins the exponent's FMA.
-  auto softmax = [&](f32x4 (&s)[NB]) __attribute__((always_inline)) {
+    // the scale is positive: the max of the raw scores gives the max of the
+    // scaled ones, and the scaling joins the exponent's FMA
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < NB; ++b) mx = fmaxf(mx, fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])));
     mx = wave_max4(mx);
     const float mn = fmaxf(m, mx * sl2);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // wave-uniform
 #pragma unroll
-    for (int r = 0; r < D / 16; ++r) acc[r] *= alpha;
+      for (int r = 0; r < D / 16; ++r) acc[r] *= alpha;
+    }
     float sum = 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -367,27 +338,47 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
     m = mn;
     pop.set(s);
   };
-  auto v_stage = [&](const T* vt) __attribute__((always_inline)) { pv_stream<T, D, NB>(acc, vt, lo, pop); };
+  auto v_stage = [&](const T* vt) __attribute__((always_inline)) {
+    const char* blk[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) blk[b] = reinterpret_cast<const char*>(vt) + 16 * b * TL::row_bytes;
+    __builtin_amdgcn_s_setprio(1);
+    pv_stream<T, D, NB, false>(acc, blk, lo, pop);
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-  // Software pipeline, one barrier per stage: stage s's softmax and value
-  // contraction run beside the score MFMAs of stage s+1, whose K is already
-  // staged.  On entering iteration s the ring holds V(s) and K(s+1) (issued
-  // one iteration earlier); the iteration then issues V(s+1) and K(s+2) into
-  // the slots of V(s-1) and K(s), both consumed before the barrier.
-  f32x4 sa[NB], sb[NB];
-  wait_dma_except<2 * NIW>();  // K(0)
-  score_band<T, D, NB>(sa, slot(IC<0>{}), lo, qf);
-  uint32_t bw[kKeyBlocks][4];  // the wave's Pbar band words (Lightweight DC)
-  // iteration s with K(s) in slot P; LAST: the final stage (no next scores;
-  // the band words load here, beside its softmax and value contraction)
-  auto iter = [&](auto pc, auto lastc, int s, f32x4 (&cur)[NB], f32x4 (&nxt)[NB]) __attribute__((always_inline)) {
+  // Stage s with its K in slot P = 2s % 4; three half-stages in flight, so
+  // each wait leaves the two younger ones pending.  Every call issues the
+  // same DMA instructions (past the last stage they read nothing), so the
+  // counts hold to the end.
+  auto chunk = [&](auto pc, int s) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
-    constexpr bool LAST = decltype(lastc)::value;
-    wait_dma_except<0>();
-    if constexpr (!LAST) {
-      issue_half(IC<P + 3>{}, 2 * s + 3);  // V(s+1)
-      if (s + 2 < NS) issue_half(IC<P + 4>{}, 2 * s + 4);  // K(s+2); workgroup-uniform
-    } else if constexpr (LDC) {
+    wait_dma_except<2 * NIW>();
+    issue_half(IC<P + 3>{}, 2 * s + 3);
+    k_stage(slot(IC<P>{}), stage_row(s));
+    wait_dma_except<2 * NIW>();
+    issue_half(IC<P + 4>{}, 2 * s + 4);
+    v_stage(slot(IC<P + 1>{}));
+  };
+  int s = 0;
+  for (; s + 2 <= NS; s += 2) {  // workgroup-uniform
+    chunk(IC<0>{}, s);
+    chunk(IC<2>{}, s + 1);
+  }
+  if (NS & 1) chunk(IC<0>{}, s);
+  wait_dma_except<0>();  // the two empty half-stages; every wave is past the loop
+
+  if constexpr (LDC) {
+    // l G Pbar V over the wave's band: the window's V rows [q0-128, q0+128)
+    // are staged again, 64 to a slot (the L2 still holds them); band block b
+    // of wave w holds keys q0 + 16w - 112 + 16b, row 16w + 16 + 16b there
+    const int lim_v = q0 + BQ < a.T ? q0 + BQ : a.T;
+    issue_rows(IC<0>{}, v, w1, lim_v);
+    issue_rows(IC<1>{}, v, w1 + R, lim_v);
+    issue_rows(IC<2>{}, v, w1 + 2 * R, lim_v);
+    issue_rows(IC<3>{}, v, w1 + 3 * R, lim_v);
+    uint32_t bw[kKeyBlocks][4];
+    {
       // word (b, 4g+i, n) of the wave's 16 x 128 band block
       const int qb = (q0 >> 4) + w, nqb = (a.T + 15) >> 4;
       const uint32_t* blk = a.band + (size_t)(qb < nqb ? qb : nqb - 1) * kBandWords;
@@ -396,60 +387,38 @@ __global__ __launch_bounds__(kANW * kWave) void attn_fwd_kernel(const AttnArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) bw[b][i] = blk[b * 256 + (4 * g + i) * 16 + n];
     }
-    mask(cur, stage_row(s));
+    wait_dma_except<0>();
+    const float f = l * gh;
+    f32x4 pb[kKeyBlocks];
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[b][i] = f * band_decode<T>(bw[b][i]);
+    BandOperand<T, kKeyBlocks> bop;
+    bop.set(pb);
+    const char* blk[kKeyBlocks];
+#pragma unroll
+    for (int b = 0; b < kKeyBlocks; ++b) {
+      const int r = 16 * w + 16 + 16 * b;  // wave-uniform, 16 .. 239
+      const char* sl = reinterpret_cast<const char*>(r < R ? slot(IC<0>{}) : r < 2 * R ? slot(IC<1>{})
+                                                             : r < 3 * R ? slot(IC<2>{}) : slot(IC<3>{}));
+      blk[b] = sl + (r % R) * TL::row_bytes;
+    }
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (!LAST) score_band<T, D, NB>(nxt, slot(IC<P + 2>{}), lo, qf);
-    softmax(cur);
-    v_stage(slot(IC<P + 1>{}));
+    pv_stream<T, D, kKeyBlocks, true>(acc, blk, lo, bop);
     __builtin_amdgcn_s_setprio(0);
-  };
-  const std::false_type mid;
-  const std::true_type last;
-  int s = 0;
-  for (; s + 2 < NS; s += 2) {  // workgroup-uniform
-    iter(IC<0>{}, mid, s, sa, sb);
-    iter(IC<2>{}, mid, s + 1, sb, sa);
-  }
-  if (NS - s == 2) {
-    iter(IC<0>{}, mid, s, sa, sb);
-    iter(IC<2>{}, last, s + 1, sb, sa);
-  } else {
-    iter(IC<0>{}, last, s, sa, sb);
-  }
-  if constexpr (LDC) {
-    // l G Pbar V over the band: block b holds keys q0 + 16w - 112 + 16b ..,
-    // window block w + 1 + b (W1's V below 8, else W2's); W1's K sat in slot
-    // PW = 2 (NS - 2) % 4, its V in PW + 1 and W2's V in PW + 3
-    auto band_tail = [&](auto pc) __attribute__((always_inline)) {
-      constexpr int PW = decltype(pc)::value;
-      const float f = l * gh;
-      f32x4 pb[kKeyBlocks];
-#pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pb[b][i] = f * band_decode<T>(bw[b][i]);
-      BandOperand<T, kKeyBlocks> bop;
-      bop.set(pb);
-      const char* blk[kKeyBlocks];
-#pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b) {
-        const int wb = w + 1 + b;  // wave-uniform
-        blk[b] = reinterpret_cast<const char*>(wb < 8 ? slot(IC<PW + 1>{}) : slot(IC<PW + 3>{})) +
-                 16 * (wb & 7) * TL::row_bytes;
-      }
-      __builtin_amdgcn_s_setprio(1);
-      pv_blocks<T, D, kKeyBlocks, true>(acc, blk, lo, bop);
-      __builtin_amdgcn_s_setprio(0);
-    };
-    if (NS & 1)
-      band_tail(IC<2>{});
-    else
-      band_tail(IC<0>{});
   }
   const float inv = 1.f / l;  // l >= the diagonal key's weight, > 0
 #pragma unroll
   for (int r = 0; r < D / 16; ++r) acc[r] *= inv;
-  store_row<T, D>(pending_rows<D>(a.o, tw, n, a.T, H, h, true, 1.f, s_xp + w * 512), acc, g, n);
+  float* xp;
+  if constexpr (kXpInRing) {
+    __syncthreads();  // every wave is done reading the ring
+    xp = reinterpret_cast<float*>(s_r0) + w * 512;
+  } else {
+    xp = s_xp + w * 512;
+  }
+  store_row<T, D>(pending_rows<D>(a.o, tw, n, a.T, H, h, true, 1.f, xp), acc, g, n);
 }
 
 template <typename T, int D>
