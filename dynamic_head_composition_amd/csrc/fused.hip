@@ -35,6 +35,22 @@ namespace ldc {
 // Run starts
 // ---------------------------------------------------------------------------
 constexpr int kRunBlock = 1024;  // tokens per run-start block (256 threads x 4)
+constexpr int kTileQ = 128;      // queries per main-attention tile
+constexpr int kStageK = 64;      // keys per main-attention stage
+constexpr int kOrderBins = 1024;  // stage-count classes of the item order
+
+// Stages of a tile before its four window stages: chunks of kStageK keys from
+// its earliest run start up to q0 - 2 kStageK.
+__device__ __forceinline__ int tile_chunks(int q0, int rs0) {
+  const int span = (q0 - 2 * kStageK) - rs0;
+  return span > 0 ? (span + kStageK - 1) / kStageK : 0;
+}
+// Order class of a tile: most chunks first (the last class holds every tile
+// with kOrderBins - 1 or more).
+__device__ __forceinline__ int order_bin(int q0, int rs0) {
+  const int c = tile_chunks(q0, rs0);
+  return kOrderBins - 1 - (c < kOrderBins - 1 ? c : kOrderBins - 1);
+}
 
 __device__ __forceinline__ int block_max_256(int x, int* red) {
   for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
@@ -53,8 +69,10 @@ __device__ __forceinline__ bool run_boundary(const int32_t* __restrict__ doc, in
 
 // last[b]: the last run boundary in tokens [1024 b, 1024 b + 1024), or -1.
 __global__ __launch_bounds__(256) void run_marks_kernel(const int32_t* __restrict__ doc, int T,
-                                                        int* __restrict__ last) {
+                                                        int* __restrict__ last, int* __restrict__ order) {
   __shared__ int red[4];
+  if (blockIdx.x == 0)  // the order histogram and cursors start at zero
+    for (int i = threadIdx.x; i < 2 * kOrderBins; i += 256) order[i] = 0;
   const int t0 = blockIdx.x * kRunBlock + 4 * threadIdx.x;
   int best = -1;
 #pragma unroll
@@ -69,7 +87,7 @@ __global__ __launch_bounds__(256) void run_marks_kernel(const int32_t* __restric
 // holds token 0's boundary) and the block's own prefix maximum up to t.
 __global__ __launch_bounds__(256) void run_starts_kernel(const int32_t* __restrict__ doc, int T,
                                                          const int* __restrict__ last,
-                                                         int* __restrict__ rs) {
+                                                         int* __restrict__ rs, int* __restrict__ order) {
   __shared__ int red[4];
   __shared__ int wtot[4];
   const int b = blockIdx.x;
@@ -101,7 +119,55 @@ __global__ __launch_bounds__(256) void run_starts_kernel(const int32_t* __restri
   before = max(before, carry);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    if (t0 + j < T) rs[t0 + j] = max(before, r[j]);
+    if (t0 + j < T) {
+      const int rsv = max(before, r[j]);
+      rs[t0 + j] = rsv;
+      // a tile's first query: count the tile in its order class
+      if (((t0 + j) & (kTileQ - 1)) == 0) atomicAdd(&order[order_bin(t0 + j, rsv)], 1);
+    }
+}
+
+// The tiles' order: tile list position = the classes before the tile's own
+// (an exclusive scan of the histogram, redone by every workgroup) + a slot
+// claimed in its class.  Tiles of one class land in any order (the order
+// only schedules work; every tile computes the same result wherever it
+// runs).
+__global__ __launch_bounds__(256) void tile_order_kernel(const int* __restrict__ rs, int T,
+                                                         int* __restrict__ order) {
+  __shared__ int base[kOrderBins];
+  __shared__ int wtot[4];
+  const int* hist = order;
+  int* cursor = order + kOrderBins;
+  int* list = order + 2 * kOrderBins;
+  int cnt[4];
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cnt[i] = hist[4 * threadIdx.x + i];
+    tot += cnt[i];
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = tot;  // inclusive scan over the wave
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wtot[w] = x;
+  __syncthreads();
+  int excl = x - tot;
+  for (int i = 0; i < w; ++i) excl += wtot[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    base[4 * threadIdx.x + i] = excl;
+    excl += cnt[i];
+  }
+  __syncthreads();
+  const int tile = blockIdx.x * 256 + threadIdx.x;
+  const int ntile = (T + kTileQ - 1) / kTileQ;
+  if (tile < ntile) {
+    const int b = order_bin(tile * kTileQ, rs[tile * kTileQ]);
+    list[base[b] + atomicAdd(&cursor[b], 1)] = tile;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -109,7 +175,8 @@ __global__ __launch_bounds__(256) void run_starts_kernel(const int32_t* __restri
 // ---------------------------------------------------------------------------
 constexpr int kANW = 8;                // waves per workgroup
 constexpr int kABQ = 16 * kANW;        // 128 queries per tile
-constexpr int kARows = 64;             // keys per stage
+constexpr int kARows = kStageK;        // keys per stage
+static_assert(kABQ == kTileQ, "the item order counts the kernel's tiles");
 constexpr int kABlocks = kARows / 16;  // 4 key blocks per stage
 
 template <int I>
@@ -205,8 +272,12 @@ __global__ __launch_bounds__(kANW * kWave, 4) void attn_fwd_kernel(const AttnArg
   const T* __restrict__ k = static_cast<const T*>(a.k);
   const T* __restrict__ v = static_cast<const T*>(a.v);
   const int H = a.H;
+  // work items (tile, head), tiles with the most stages first
   const int item = blockIdx.x;
-  const int tile = item / H, h = item - tile * H;
+  const int slot_i = item / H, h = item - slot_i * H;
+  const int ntile = (a.T + BQ - 1) / BQ;
+  int tile = __builtin_amdgcn_readfirstlane(a.order[slot_i]);
+  tile = tile < 0 ? 0 : tile < ntile ? tile : ntile - 1;  // the list is a permutation; kept in range regardless
   const int q0 = tile * BQ;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, n = lane & 15;
@@ -227,8 +298,7 @@ __global__ __launch_bounds__(kANW * kWave, 4) void attn_fwd_kernel(const AttnArg
   // stages: chunks of R keys from (at or before) ks0 up to q0-129, then the
   // four window stages [q0-128, q0+128)
   const int w1 = q0 - 2 * R;
-  const int span = w1 - ks0;
-  const int nc = span > 0 ? (span + R - 1) / R : 0;
+  const int nc = tile_chunks(q0, ks0);
   const int NS = nc + 4;
   auto stage_row = [&](int s) __attribute__((always_inline)) { return w1 - R * (nc - s); };
   auto slot = [&](auto c) __attribute__((always_inline)) -> T* {
@@ -434,12 +504,19 @@ static hipError_t launch_attn(const AttnArgs& a, bool ldc, hipStream_t st) {
 
 size_t run_blocks(int64_t T) { return (size_t)((T + kRunBlock - 1) / kRunBlock); }
 
-hipError_t run_starts_dispatch(const int32_t* doc, int T, int* last, int* rs, hipStream_t st) {
+size_t order_ints(int64_t T) { return 2 * kOrderBins + (size_t)((T + kTileQ - 1) / kTileQ); }
+int order_list_offset() { return 2 * kOrderBins; }
+
+hipError_t run_starts_dispatch(const int32_t* doc, int T, int* last, int* rs, int* order, hipStream_t st) {
   const int nb = (int)run_blocks(T);
-  hipLaunchKernelGGL(run_marks_kernel, dim3(nb), dim3(256), 0, st, doc, T, last);
+  hipLaunchKernelGGL(run_marks_kernel, dim3(nb), dim3(256), 0, st, doc, T, last, order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(run_starts_kernel, dim3(nb), dim3(256), 0, st, doc, T, last, rs);
+  hipLaunchKernelGGL(run_starts_kernel, dim3(nb), dim3(256), 0, st, doc, T, last, rs, order);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ntile = (T + kTileQ - 1) / kTileQ;
+  hipLaunchKernelGGL(tile_order_kernel, dim3((ntile + 255) / 256), dim3(256), 0, st, rs, T, order);
   return hipGetLastError();
 }
 

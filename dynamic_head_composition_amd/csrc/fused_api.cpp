@@ -26,7 +26,9 @@ int check(int dtype, int64_t T, int H, int d, int window, float scale) {
 }
 
 // run-start arrays: the block summaries, then one int per token
-size_t runs_bytes(int64_t T) { return room(ldc::run_blocks(T) * 4) + (size_t)T * 4; }
+size_t runs_bytes(int64_t T) {
+  return room(ldc::run_blocks(T) * 4) + room((size_t)T * 4) + ldc::order_ints(T) * 4;
+}
 
 int run(bool ldc_on, int dtype, int64_t T, int H, int d, int window, float scale, const void* q,
         const void* k, const void* v, const float* c, const float* g, const int32_t* doc_ids, float* o,
@@ -58,8 +60,9 @@ int run(bool ldc_on, int dtype, int64_t T, int H, int d, int window, float scale
   }
   int* last = reinterpret_cast<int*>(ws);
   int* rs = reinterpret_cast<int*>(ws + room(ldc::run_blocks(T) * 4));
-  if (ldc::run_starts_dispatch(doc_ids, (int)T, last, rs, hs) != hipSuccess) return LDC_ERR_HIP;
-  ldc::AttnArgs a{(int)T, H, scale, q, k, v, g, band, rs, o};
+  int* order = reinterpret_cast<int*>(ws + room(ldc::run_blocks(T) * 4) + room((size_t)T * 4));
+  if (ldc::run_starts_dispatch(doc_ids, (int)T, last, rs, order, hs) != hipSuccess) return LDC_ERR_HIP;
+  ldc::AttnArgs a{(int)T, H, scale, q, k, v, g, band, rs, order + ldc::order_list_offset(), o};
   return ldc::attn_fwd_dispatch(d, a, ldc_on, hs) == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
 

@@ -31,7 +31,9 @@
  * d, window) bytes of the fused call's workspace receive the Lightweight DC
  * layer's saved state exactly as ldc_fwd writes it (the composed-map band
  * and the softmax statistics), so it can be passed to ldc_bwd as `saved`
- * until the next call that writes it; the rest holds every token's run start.
+ * until the next call that writes it; the rest holds every token's run start
+ * and the order in which the main attention takes its 128-query tiles (most
+ * key stages first, so that long documents' tiles do not trail at the end).
  * Too small or missing: LDC_ERR_WORKSPACE.
  */
 #ifndef LDC_FUSED_H_
