@@ -462,30 +462,32 @@ def bench_dcmha(args):
 FUSED_METRIC = "attention block fwd tokens/s on 1 MI355X (GPT-2-small shape): main attention + LDC fused"
 FUSED_SOURCES = ("ldc_device.hpp", "ldc_pipeline.hpp", "ldc_fwd.hip", "ldc_internal.h", "fused.hip",
                  "fused_internal.h")
-FUSED_TILE = 128  # queries per work item of the main attention kernel (and keys per stage)
+FUSED_TILE = 128   # queries per work item of the main attention kernel
+FUSED_STAGE = 64   # keys per stage
 
 
 def fused_design_bytes(doc: np.ndarray, H: int, d: int, elem: int) -> int:
     """Bytes the fused call moves as designed, with no reuse between work
     items: the Lightweight DC score pass (Q, K, C, G, doc in; the band and the
-    statistics out), the run starts (doc in, one int per token out), and per
-    (128-query tile, head) item its Q rows, every 128-key stage of K and V
-    from the tile's earliest run start to its last query, its G, run starts
-    and band blocks, and its float32 O rows.  Halo and document-prefix rows
-    that neighbouring items share come from the L2, so measured HBM traffic
-    lies between the algorithmic bytes and this figure."""
+    statistics out), the run starts and the item order (doc in, one int per
+    token out), and per (128-query tile, head) item its Q rows, every 64-key
+    stage of K and V from the tile's earliest run start to its last query,
+    the window's 256 V rows staged again for the band's value contraction,
+    its G, run starts and band blocks, and its float32 O rows.  Rows that
+    neighbouring items share come from the L2, so measured HBM traffic lies
+    between the algorithmic bytes and this figure."""
     T = len(doc)
     row = H * d
     starts = np.ones(T, dtype=bool)
     starts[1:] = doc[1:] != doc[:-1]
     rs = np.maximum.accumulate(np.where(starts, np.arange(T), 0))
     q0 = np.arange(0, T, FUSED_TILE)
-    span = (q0 - FUSED_TILE) - rs[q0]
-    stages = np.where(span > 0, (span + FUSED_TILE - 1) // FUSED_TILE, 0) + 2
+    span = (q0 - 2 * FUSED_STAGE) - rs[q0]
+    stages = np.where(span > 0, (span + FUSED_STAGE - 1) // FUSED_STAGE, 0) + 4
     score_pass = T * (2 * row * elem + 8 * H + 4 + 512 + 8 * H)
     run_starts = T * 12
-    per_item_rows = int(stages.sum()) * 2 * FUSED_TILE * d * elem  # K and V stages, one head
-    attention = H * per_item_rows + T * (row * elem + 4 * H + 4 * H + 512 * H + row * 4)
+    per_head_rows = (int(stages.sum()) * 2 * FUSED_STAGE + len(q0) * 256) * d * elem  # K and V stages, restage
+    attention = H * per_head_rows + T * (row * elem + 4 * H + 4 * H + 512 * H + row * 4)
     return int(score_pass + run_starts + attention)
 
 
