@@ -261,6 +261,28 @@ def copy_probe(mib: int) -> None:
     del src, dst
 
 
+def copy_bandwidth(mib: int = 1024, reps: int = 10) -> dict:
+    """Achievable HBM bandwidth of a plain device copy (read + write) of `mib`
+    MiB on this GPU, median of `reps` copies timed with events: the practical
+    ceiling beside the 8 TB/s peak.  Run after the timed steps."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
+    moved = 2 * (mib << 20)
+    del src, dst
+    return {"GBps": round(moved / (ms * 1e-3) / 1e9, 1), "bytes_per_copy": moved,
+            "frac_of_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def mudd_bytes_per_token(dm: int, W: int, J: int, elem: int) -> dict:
     """Compulsory HBM bytes per token of the two MUDD kernels."""
     return {
@@ -948,6 +970,8 @@ def main():
         "passes": passes,
         "kernels": per_kernel,
     }
+    # after the timed steps: the achievable HBM rate of a plain copy on this GPU
+    line["hbm_copy_probe"] = copy_bandwidth()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
