@@ -249,8 +249,9 @@ __device__ __forceinline__ void pv_stream(f32x4 (&acc)[D / 16], const char* cons
 
 // One workgroup per (128-query tile, head).  Two workgroups share a CU: the
 // ring (four 64-key slots) is 64 KB at d = 128 and the kernel keeps to 128
-// VGPRs, so each SIMD holds four waves.
-template <typename T, int D, bool LDC>
+// VGPRs, so each SIMD holds four waves.  NBB: key blocks of the Lightweight
+// DC band (8 for windows up to 113 keys, 10 up to 128).
+template <typename T, int D, bool LDC, int NBB = kKeyBlocks>
 __global__ __launch_bounds__(kANW * kWave, 4) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NW = kANW, BQ = kABQ, R = kARows, NB = kABlocks;
   constexpr int NIW = tile_insts_per_wave<T, D, R, NW>();  // DMA instructions per wave per half-stage
@@ -267,6 +268,9 @@ __global__ __launch_bounds__(kANW * kWave, 4) void attn_fwd_kernel(const AttnArg
   // slot holds it (d = 128), else an array of its own
   constexpr bool kXpInRing = R * D * (int)sizeof(T) >= NW * 512 * (int)sizeof(float);
   __shared__ __attribute__((aligned(16))) float s_xp[kXpInRing ? 4 : NW * 512];
+  // a 10-block band reaches 16 rows below the window stages: those V rows
+  constexpr int kExRows = NBB > kKeyBlocks ? 16 * (NBB - kKeyBlocks) / 2 : 1;
+  __shared__ __attribute__((aligned(1024))) T s_ex[kExRows * D];
 
   const T* __restrict__ q = static_cast<const T*>(a.q);
   const T* __restrict__ k = static_cast<const T*>(a.k);
@@ -440,42 +444,63 @@ __global__ __launch_bounds__(kANW * kWave, 4) void attn_fwd_kernel(const AttnArg
 
   if constexpr (LDC) {
     // l G Pbar V over the wave's band: the window's V rows [q0-128, q0+128)
-    // are staged again, 64 to a slot (the L2 still holds them); band block b
-    // of wave w holds keys q0 + 16w - 112 + 16b, row 16w + 16 + 16b there
+    // are staged again, 64 to a slot (the L2 still holds them), and for a
+    // 10-block band the 16 rows below them into s_ex; band block b of wave w
+    // holds keys q0 + 16w - 16 (NBB - 1) + 16b, row r = 16w + 16b + 16 (9 -
+    // NBB) of the window (r = -16: s_ex)
+    static_assert(NBB == kKeyBlocks || NBB == kKeyBlocks + 2, "8- or 10-block bands");
     const int lim_v = q0 + BQ < a.T ? q0 + BQ : a.T;
     issue_rows(IC<0>{}, v, w1, lim_v);
     issue_rows(IC<1>{}, v, w1 + R, lim_v);
     issue_rows(IC<2>{}, v, w1 + 2 * R, lim_v);
     issue_rows(IC<3>{}, v, w1 + 3 * R, lim_v);
-    uint32_t bw[kKeyBlocks][4];
+    if constexpr (NBB > kKeyBlocks) {
+      // rows [q0-144, q0-128): RPI rows per DMA instruction, one instruction
+      // for each of the first 16 / RPI waves (rows below 0 read as zero)
+      constexpr int NI16 = 16 / RPI;
+      if (w < NI16) {  // wave-uniform
+        const int row0 = w1 - 16;
+        const int sr = row0 + w * RPI + lane / TL::chunks;
+        const int lo_r = row0 > 0 ? row0 : 0;
+        const int hi_r = row0 + 16 < lim_v ? row0 + 16 : lim_v;
+        const uint32_t bytes = hi_r > lo_r ? (uint32_t)(hi_r - 1 - lo_r) * rstride + D * sizeof(T) : 0u;
+        const i32x4 rsrc = make_rsrc(v + ((size_t)(hi_r > lo_r ? lo_r : 0) * H + h) * D, bytes);
+        const int rl = w * RPI + lane / TL::chunks;  // row within the 16
+        const uint32_t vo = (sr >= lo_r && sr < hi_r)
+                                ? (uint32_t)(sr - lo_r) * rstride + (uint32_t)TL::pos(rl, lane % TL::chunks) * 16u
+                                : bytes;
+        ldc_buffer_load_lds(rsrc, (lds_u32_ptr)(reinterpret_cast<char*>(s_ex) + w * 1024), 16, (int)vo, 0, 0, 0);
+      }
+    }
+    uint32_t bw[NBB][4];
     {
-      // word (b, 4g+i, n) of the wave's 16 x 128 band block
+      // word (b, 4g+i, n) of the wave's 16 x 16NBB band block
       const int qb = (q0 >> 4) + w, nqb = (a.T + 15) >> 4;
-      const uint32_t* blk = a.band + (size_t)(qb < nqb ? qb : nqb - 1) * kBandWords;
+      const uint32_t* blk = a.band + (size_t)(qb < nqb ? qb : nqb - 1) * band_words<NBB>();
 #pragma unroll
-      for (int b = 0; b < kKeyBlocks; ++b)
+      for (int b = 0; b < NBB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) bw[b][i] = blk[b * 256 + (4 * g + i) * 16 + n];
     }
     wait_dma_except<0>();
     const float f = l * gh;
-    f32x4 pb[kKeyBlocks];
+    f32x4 pb[NBB];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b)
+    for (int b = 0; b < NBB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[b][i] = f * band_decode<T>(bw[b][i]);
-    BandOperand<T, kKeyBlocks> bop;
+    BandOperand<T, NBB> bop;
     bop.set(pb);
-    const char* blk[kKeyBlocks];
+    const char* blk[NBB];
 #pragma unroll
-    for (int b = 0; b < kKeyBlocks; ++b) {
-      const int r = 16 * w + 16 + 16 * b;  // wave-uniform, 16 .. 239
-      const char* sl = reinterpret_cast<const char*>(r < R ? slot(IC<0>{}) : r < 2 * R ? slot(IC<1>{})
-                                                             : r < 3 * R ? slot(IC<2>{}) : slot(IC<3>{}));
-      blk[b] = sl + (r % R) * TL::row_bytes;
+    for (int b = 0; b < NBB; ++b) {
+      const int r = 16 * w + 16 * b + 16 * (9 - NBB);  // wave-uniform, -16 .. 239
+      const char* sl = reinterpret_cast<const char*>(r < 0 ? s_ex : r < R ? slot(IC<0>{}) : r < 2 * R ? slot(IC<1>{})
+                                                     : r < 3 * R ? slot(IC<2>{}) : slot(IC<3>{}));
+      blk[b] = sl + (r < 0 ? 0 : r % R) * TL::row_bytes;
     }
     __builtin_amdgcn_s_setprio(1);
-    pv_stream<T, D, kKeyBlocks, true>(acc, blk, lo, bop);
+    pv_stream<T, D, NBB, true>(acc, blk, lo, bop);
     __builtin_amdgcn_s_setprio(0);
   }
   const float inv = 1.f / l;  // l >= the diagonal key's weight, > 0
@@ -495,7 +520,9 @@ template <typename T, int D>
 static hipError_t launch_attn(const AttnArgs& a, bool ldc, hipStream_t st) {
   const int ntile = (a.T + kABQ - 1) / kABQ;
   const dim3 grid(ntile * a.H), block(kANW * kWave);
-  if (ldc)
+  if (ldc && a.window > kMaxWindow)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, true, kKeyBlocks + 2>), grid, block, 0, st, a);
+  else if (ldc)
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), grid, block, 0, st, a);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), grid, block, 0, st, a);

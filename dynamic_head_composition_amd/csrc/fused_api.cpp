@@ -18,7 +18,7 @@ size_t room(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int check(int dtype, int64_t T, int H, int d, int window, float scale) {
   if (dtype != LDC_BF16 && dtype != LDC_F32) return LDC_ERR_DTYPE;
-  if (T < 0 || H < 1 || window < 1 || window > 113 || d < 1 || !scale_ok(scale)) return LDC_ERR_SHAPE;
+  if (T < 0 || H < 1 || window < 1 || window > 128 || d < 1 || !scale_ok(scale)) return LDC_ERR_SHAPE;
   const int64_t elems = T * (int64_t)H * (int64_t)d;
   if (T > (int64_t)1 << 30 || elems + 512LL * H * d >= ((int64_t)1 << 31)) return LDC_ERR_SHAPE;
   if (dtype != LDC_BF16 || !(d == 64 || d == 128)) return LDC_ERR_UNSUPPORTED;
@@ -62,7 +62,7 @@ int run(bool ldc_on, int dtype, int64_t T, int H, int d, int window, float scale
   int* rs = reinterpret_cast<int*>(ws + room(ldc::run_blocks(T) * 4));
   int* order = reinterpret_cast<int*>(ws + room(ldc::run_blocks(T) * 4) + room((size_t)T * 4));
   if (ldc::run_starts_dispatch(doc_ids, (int)T, last, rs, order, hs) != hipSuccess) return LDC_ERR_HIP;
-  ldc::AttnArgs a{(int)T, H, scale, q, k, v, g, band, rs, order + ldc::order_list_offset(), o};
+  ldc::AttnArgs a{(int)T, H, window, scale, q, k, v, g, band, rs, order + ldc::order_list_offset(), o};
   return ldc::attn_fwd_dispatch(d, a, ldc_on, hs) == hipSuccess ? LDC_OK : LDC_ERR_HIP;
 }
 

@@ -8,6 +8,7 @@ namespace ldc {
 
 struct AttnArgs {
   int T, H;
+  int window;             // the Lightweight DC window (its band: 8 blocks up to 113 keys, else 10)
   float scale;
   const void *q, *k, *v;
   const float* g;         // Lightweight DC scale G [T,H] (with the band)

@@ -20,7 +20,7 @@
  * float32 (written, never read); device pointers owned by the caller, 16-byte
  * aligned; the call only enqueues work on `stream` (NULL: the default stream)
  * and allocates nothing.  Supported: d in {64, 128}; H >= 1;
- * 1 <= window <= 113; T >= 0 (T == 0 is a no-op); T*H*d < 2^31.  Arguments are
+ * 1 <= window <= 128; T >= 0 (T == 0 is a no-op); T*H*d < 2^31.  Arguments are
  * validated before any HIP call; errors return a non-zero ldc_status with no
  * side effects.  The main attention's work grows with the document length
  * (every query reads its whole run).

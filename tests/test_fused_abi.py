@@ -36,7 +36,7 @@ def test_workspace_sizes():
         assert fz.main_workspace_bytes(T) == runs(T)
     assert fz.workspace_bytes(ldc.LDC_BF16, 0, 6, 128) == 0
     assert fz.workspace_bytes(ldc.LDC_F32, 100, 6, 64) == 0      # bf16 only
-    assert fz.workspace_bytes(ldc.LDC_BF16, 100, 6, 128, 114) == 0
+    assert fz.workspace_bytes(ldc.LDC_BF16, 100, 6, 128, 129) == 0
     assert fz.main_workspace_bytes(0) == 0
 
 
@@ -61,7 +61,7 @@ def test_fused_validation():
     assert fused(dtype=2) == 3                      # not a dtype
     assert fused(T=-1) == 2
     assert fused(H=0) == 2
-    assert fused(window=0) == 2 and fused(window=114) == 2
+    assert fused(window=0) == 2 and fused(window=129) == 2
     assert fused(scale=0.0) == 2 and fused(scale=float("inf")) == 2
     assert fused(T=1 << 24, H=6, d=128) == 2      # T*H*d beyond int32
     assert fused(dtype=ldc.LDC_F32, d=64) == 5    # bf16 only

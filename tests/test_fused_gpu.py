@@ -27,6 +27,11 @@ SMALL = [  # (T, H, d, window, docs, seed, c_kind)
     (456, 6, 64, 112, ("fixed", REPEATED), 8, "normal0.5"),      # a repeated id is a new document
     (129, 7, 128, 112, ("geometric", 40), 9, "normal0.5"),     # H = 7
     (len(EDGES), 2, 64, 112, ("fixed", EDGES), 10, "normal0.5"),
+    # windows of 114-128 keys: the 10-block band, whose first block lies below the window stages
+    (1100, 3, 128, 128, ("geometric", 300), 11, "normal0.5"),
+    (700, 2, 64, 114, ("uniform", 8, 256), 12, "normal1neg"),
+    (2049, 6, 128, 120, ("geometric", 1024), 13, "onehot80"),
+    (150, 1, 64, 128, ("single",), 14, "normal0.5"),
 ]
 
 
@@ -128,12 +133,13 @@ def test_empty(fz):
     assert fz.main_fwd(q, q, q, doc).shape == (0, 6, 128)
 
 
-def test_saved_state_matches_layer_forward(fz, ldc):
+@pytest.mark.parametrize("window", [112, 128])
+def test_saved_state_matches_layer_forward(fz, ldc, window):
     """The fused call's workspace holds the Lightweight DC layer's saved state
     exactly as ldc_fwd writes it (the same score pass), so the backward can
     take it."""
     import torch
-    w = wl.make_workload(777, 6, 128, docs=("geometric", 200), seed=33, with_do=False)
+    w = wl.make_workload(777, 6, 128, window=window, docs=("geometric", 200), seed=33, with_do=False)
     q, k, v, c, g, doc = inputs(w)
     _, saved = fz.fwd(q, k, v, c, g, doc, window=w.window, scale=w.scale, save=True)
     _, ref = ldc.fwd(q, k, v, c, g, doc, window=w.window, scale=w.scale, save=True)
