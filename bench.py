@@ -547,6 +547,9 @@ def bench_fused(args):
         raise SystemExit("no GPU visible")
     log("generating workload 1 ...")
     w = wl.config_workload(1, T=args.tokens)
+    if args.window:
+        w.window = args.window
+        w.name += f"_win{args.window}"
     x = w.torch_inputs("cuda", with_do=False)
     T, H, d = w.T, w.H, w.d
     elem = 2 if w.dtype == "bf16" else 4
@@ -843,6 +846,9 @@ def main():
                          "mudd: MUDD layer mixing; fused: the block's main attention with the "
                          "Lightweight DC layer fused in (forward)")
     ap.add_argument("--tokens", type=int, default=None, help="truncate the stream (quick runs only)")
+    ap.add_argument("--window", type=int, default=None,
+                    help="another Lightweight DC window (1-128) on the same stream, for the ldc and "
+                         "fused workloads (not the headline configuration)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -874,6 +880,9 @@ def main():
 
     log(f"generating workload {args.config} ...")
     w = wl.config_workload(args.config, T=args.tokens)
+    if args.window:
+        w.window = args.window
+        w.name += f"_win{args.window}"
     x = w.torch_inputs("cuda")
     T, H, d = w.T, w.H, w.d
     elem = 2 if w.dtype == "bf16" else 4
