@@ -48,6 +48,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m dynamic_head_composition_amd.build`")
+    # torch first: its HIP runtime is then the one libldc.so binds to, so the
+    # streams and device memory torch hands over belong to the runtime that
+    # launches the kernels (loading the library first, then torch, left the
+    # launches failing with LDC_ERR_HIP in one process)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.ldc_fwd.argtypes = [i32, i64, i32, i32, i32, f32] + [vp] * 7 + [vp, sz, vp]
